@@ -1,0 +1,129 @@
+"""Pins for the oracle's fixed-size cache layout and ring bookkeeping
+(companion page: "Fixed-Size Cache Layout", "Ring Buffer vs. Naive Slicing",
+"Why This Wasn't Already Standard")."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from kv_cache_compression_obs_amd import synth
+from oracle import CacheState, Config, decode_step, prefill_compress_one, ring_slot
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")
+
+
+def _cfg(**kw):
+    base = dict(n_q_heads=4, n_kv_heads=2, d_qk=8, d_v=8, L_sink=3, K=5, L_recent=6,
+                W=4, pool=3)
+    base.update(kw)
+    return Config(**base)
+
+
+def _inputs(cfg, L, seed=0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((cfg.n_q_heads, cfg.W, cfg.d_qk))
+    k = rng.standard_normal((cfg.n_kv_heads, L, cfg.d_qk))
+    v = rng.standard_normal((cfg.n_kv_heads, L, cfg.d_v))
+    return q, k, v
+
+
+@pytest.mark.parametrize("L", [1, 7, 13, 14, 15, 28, 71])
+def test_cache_shape_is_fixed_and_prefix_valid(L):
+    cfg = _cfg()
+    C = cfg.C                      # 14
+    res = prefill_compress_one(cfg, *_inputs(cfg, L))
+    assert res.k_cache.shape == (2, C, 8) and res.v_cache.shape == (2, C, 8)
+    assert res.slot_pos.shape == (2, C)
+    n_valid = min(L, C)
+    assert (res.slot_pos[:, :n_valid] >= 0).all()
+    assert (res.slot_pos[:, n_valid:] == -1).all()
+    for h in range(2):
+        used = res.slot_pos[h, :n_valid]
+        assert len(set(used.tolist())) == n_valid          # every position at most once
+
+
+@pytest.mark.parametrize("L", [15, 16, 19, 20, 27, 71])
+def test_compressed_layout_closed_form(L):
+    cfg = _cfg()
+    S, K, R = cfg.L_sink, cfg.K, cfg.L_recent
+    q, k, v = _inputs(cfg, L, seed=L)
+    res = prefill_compress_one(cfg, q, k, v)
+    for h in range(2):
+        sp = res.slot_pos[h]
+        np.testing.assert_array_equal(sp[:S], np.arange(S))                 # sinks kept
+        np.testing.assert_array_equal(sp[S:S + K], S + res.sel[h])           # ascending top-K
+        assert np.all(np.diff(sp[S:S + K]) > 0)
+        assert sorted(sp[S + K:].tolist()) == list(range(L - R, L))          # last R tokens
+        for t in range(L - R, L):                                            # ring phase
+            assert sp[S + K + (t - S - K) % R] == t
+        # rows are bit-exact copies of the inputs they name
+        np.testing.assert_array_equal(res.k_cache[h], k[h, sp])
+        np.testing.assert_array_equal(res.v_cache[h], v[h, sp])
+
+
+@pytest.mark.parametrize("L", [1, 9, 14])
+def test_uncompressed_prompt_lays_out_as_identity(L):
+    cfg = _cfg()
+    res = prefill_compress_one(cfg, *_inputs(cfg, L))
+    for h in range(2):
+        np.testing.assert_array_equal(res.slot_pos[h, :L], np.arange(L))
+    assert res.sel is None
+    for t in range(L):
+        assert ring_slot(t, cfg.L_sink, cfg.K, cfg.L_recent) == t
+
+
+@pytest.mark.parametrize("L", [5, 20])
+def test_decode_rotates_only_the_recent_window(L):
+    # after the step at position t the ring holds exactly t-R+1 .. t (once it
+    # has filled), every write evicts exactly t-R, and no other slot changes
+    cfg = _cfg()
+    S, K, R, C = cfg.L_sink, cfg.K, cfg.L_recent, cfg.C
+    rng = np.random.default_rng(L)
+    state = CacheState(cfg, 1)
+    q, k, v = _inputs(cfg, L, seed=3)
+    state.admit(0, prefill_compress_one(cfg, q, k, v))
+    for t in range(L, L + 3 * R + 2):
+        before = state.slot_pos[0].copy()
+        decode_step(state, rng.standard_normal((1, 4, 8)), rng.standard_normal((1, 2, 8)),
+                    rng.standard_normal((1, 2, 8)), np.array([t]))
+        after = state.slot_pos[0]
+        changed = np.nonzero((before != after).any(axis=0))[0]
+        assert len(changed) == 1
+        s = int(changed[0])
+        assert s == (t if t < S + K else S + K + (t - S - K) % R)
+        assert (after[:, s] == t).all()
+        if t >= C:
+            assert (before[:, s] == t - R).all()                             # evicts t - R
+            assert sorted(after[0, S + K:].tolist()) == list(range(t - R + 1, t + 1))
+        assert state.n_tokens[0] == t + 1
+
+
+def test_pages_constants_fix_the_128k_to_32k_cache():
+    gold = json.load(open(GOLDEN))
+    L, C = gold["context_tokens"]["value"], gold["fixed_cache_tokens"]["value"]
+    assert L / C == gold["kv_memory_reduction"]["value"]
+    for name in ("llama8b_128k", "deepseek_mla_128k"):
+        w = synth.workload(name)
+        assert w["C"] == C and w["L"] == L
+        assert w["L_recent"] == gold["deepseek_L_recent"]["value"]
+        # KV bytes of the fixed cache vs the uncompressed prompt: exactly L / C
+        cfg = Config(n_q_heads=w["n_q_heads"], n_kv_heads=w["n_kv_heads"], d_qk=w["d_qk"],
+                     d_v=w["d_v"], L_sink=w["L_sink"], K=w["K"], L_recent=w["L_recent"],
+                     W=w["W"], pool=w["pool"], v_aliases_k=w["v_aliases_k"])
+        assert cfg.C * 4 == L
+
+
+def test_tiny_workload_regression_fixture():
+    # stored by tests/golden/make_golden.py (oracle + seeded inputs only)
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "tiny_fp32_prefill.json")))
+    w = synth.workload("tiny_fp32")
+    cfg = Config(n_q_heads=4, n_kv_heads=2, d_qk=64, d_v=64, L_sink=4, K=64, L_recent=128,
+                 W=16, pool=7)
+    inp = synth.prefill_inputs(w, seed=1)
+    q, k, v = (synth.to_f64(inp[n])[0] for n in ("q_obs", "k", "v"))
+    res = prefill_compress_one(cfg, q, k, v)
+    np.testing.assert_array_equal(res.sel, gold["sel"])
+    np.testing.assert_array_equal(res.slot_pos, gold["slot_pos"])
+    np.testing.assert_allclose(res.raw.sum(axis=1), gold["raw_sum"], rtol=1e-12)
