@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the SnapStream hot path on one MI355X.
+
+One step = one ss_prefill_compress of the whole batch (one layer) followed by
+the workload's decode steps (ss_decode_step), all inputs already resident in
+HBM.  Default workload: Llama-3.1-8B-shaped layer, bf16, 32q/8kv heads, d 128,
+batch 16, 16384-token prompts compressed to C = 4096 (64 + 1984 + 2048),
+W = 32, pool 7, RoPE 5e5, 256 decode steps.
+
+Decode runs over `--replicas` distinct copies of the layer's cache in turn
+(step t uses copy t mod replicas), so consecutive decode steps do not find
+the previous step's cache in the 256 MB Infinity Cache; each copy keeps its
+own sequence position.
+
+Prints one JSON line.  `value` = algorithmic HBM bytes of the step (prefill:
+prompt keys read once + C cache rows gathered, read and written; decode: every
+valid cache row read) per second of wall time.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn HBM GB/s + tokens/s over fixed cache; prefill compress ms/layer"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (plumbing for the library's timed entry points)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+def algorithmic_bytes(w, elem):
+    B, Hkv, d, dv, L, C = w["B"], w["n_kv_heads"], w["d_qk"], w["d_v"], w["L"], w["C"]
+    row = (d + (0 if w["v_aliases_k"] else dv)) * elem
+    decode = B * Hkv * min(L, C) * row                       # every valid slot read once
+    prefill = B * Hkv * L * d * elem + 2 * B * Hkv * min(L, C) * row
+    return prefill, decode
+
+
+def score_flops(w):
+    """Q_obs.K^T flops of the two score passes per layer: pass 1 over all L
+    keys, pass 2 over the m middle keys (algorithmic = pass 1 only)."""
+    B, Hq, d, W, L = w["B"], w["n_q_heads"], w["d_qk"], w["W"], w["L"]
+    m = L - w["L_sink"] - w["L_recent"]
+    rows = B * Hq * W
+    return 2.0 * rows * d * L, 2.0 * rows * d * (L + m)
+
+
+def cpu_baseline(w, inp, dec, budget_s=12.0):
+    """The oracle, untuned, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    from kv_cache_compression_obs_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    cfg = oracle.Config(n_q_heads=w["n_q_heads"], n_kv_heads=w["n_kv_heads"], d_qk=w["d_qk"],
+                        d_v=w["d_v"], L_sink=w["L_sink"], K=w["K"], L_recent=w["L_recent"],
+                        W=w["W"], pool=w["pool"], v_aliases_k=w["v_aliases_k"],
+                        rope_theta=w["rope_theta"], rope_begin=w["rope_begin"],
+                        rope_end=w["rope_end"], dtype=w["dtype"])
+    elem = 2 if w["dtype"] == "bf16" else 4
+    pre_b, dec_b = algorithmic_bytes(dict(w, B=1), elem)
+    t0 = time.perf_counter()
+    n_req = 0
+    results = []
+    while n_req < w["B"] and (time.perf_counter() - t0) < budget_s / 2:
+        q = synth.to_f64(inp["q_obs"][n_req])
+        k = synth.to_f64(inp["k"][n_req])
+        v = synth.to_f64(inp["v"][n_req]) if inp["v"] is not None else None
+        results.append(oracle.prefill_compress_one(cfg, q, k, v))
+        n_req += 1
+    t_pre = time.perf_counter() - t0
+    state = oracle.CacheState(cfg, n_req)
+    for i, r in enumerate(results):
+        state.admit(i, r)
+    t1 = time.perf_counter()
+    n_dec = 0
+    while n_dec < dec["q"].shape[0] and (time.perf_counter() - t1) < budget_s / 2:
+        sl = slice(0, n_req)
+        oracle.decode_step(state, synth.to_f64(dec["q"][n_dec][sl]),
+                           synth.to_f64(dec["k_new"][n_dec][sl]),
+                           synth.to_f64(dec["v_new"][n_dec][sl]) if dec["v_new"] is not None
+                           else None, np.full(n_req, w["L"] + n_dec))
+        n_dec += 1
+    t_dec = time.perf_counter() - t1
+    sample_bytes = n_req * pre_b + n_dec * n_req * dec_b
+    return {
+        "value": sample_bytes / (t_pre + t_dec) / 1e9,
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle: prefill compression of {n_req} of {w['B']} requests "
+                   f"({t_pre:.2f} s), then {n_dec} decode steps over those {n_req} rows "
+                   f"({t_dec:.2f} s); same algorithmic-byte accounting as value"),
+        "prefill_compress_ms_per_request": 1e3 * t_pre / max(n_req, 1),
+        "decode_ms_per_row_step": 1e3 * t_dec / max(n_dec * n_req, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b_c4k")
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this library runs on one GPU "
+              "(the multi-GPU sharding is a design note, not a code path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_compression_obs_amd import snapstream as ss
+    from kv_cache_compression_obs_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = synth.workload(args.workload)
+    cfg = ss.make_config(**w)
+    B, Hq, L, C = w["B"], w["n_q_heads"], w["L"], w["C"]
+    n_dec = args.decode_steps or w["steps"]
+    R = max(1, args.replicas)
+    elem = 2 if w["dtype"] == "bf16" else 4
+    dt = synth.TORCH_DTYPE[w["dtype"]]
+
+    inp = synth.prefill_inputs(w, seed=2, device="cuda")
+    dec = synth.decode_inputs(w, seed=2, steps=n_dec, device="cuda")
+    caches = [ss.Cache(cfg, B) for _ in range(R)]
+    ws_p = torch.empty(ss.ss_prefill_workspace_bytes(cfg, B, L), dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(ss.ss_decode_workspace_bytes(cfg, B), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, w["d_v"], dtype=dt, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    total_steps = args.warmup + args.steps
+    max_pos = total_steps * n_dec + 1
+    posbuf = (L + torch.arange(max_pos, dtype=torch.int32, device="cuda"))[:, None].repeat(1, B)
+    for c in caches:                       # every copy starts as a compressed prompt
+        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], c, ws=ws_p)
+    count = [0] * R
+
+    hip = HipEvents()
+    ev_score = [hip.create(2) for _ in range(total_steps)]
+    ev_attn = [hip.create(2 * n_dec) for _ in range(total_steps)]
+    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total_steps)]
+
+    def step(i):
+        e = tev[i]
+        e[0].record()
+        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], caches[0], ws=ws_p,
+                               events=(ev_score[i][0], ev_score[i][1]))
+        count[0] = 0
+        e[1].record()
+        ea = ev_attn[i]
+        for t in range(n_dec):
+            r = t % R
+            vn = dec["v_new"][t] if dec["v_new"] is not None else None
+            ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], vn, posbuf[count[r]], caches[r],
+                              out, err, ws_d, events=(ea[2 * t], ea[2 * t + 1]))
+            count[r] += 1
+        e[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(err.item()) != 0:
+        raise RuntimeError("decode reported pos != n_tokens: the benchmark's bookkeeping is wrong")
+
+    timed = range(args.warmup, total_steps)
+    pre_ms = [tev[i][0].elapsed_time(tev[i][1]) for i in timed]
+    dec_ms = [tev[i][1].elapsed_time(tev[i][2]) for i in timed]
+    score_ms = [hip.elapsed_ms(ev_score[i][0], ev_score[i][1]) for i in timed]
+    attn_ms = [hip.elapsed_ms(ev_attn[i][2 * t], ev_attn[i][2 * t + 1])
+               for i in timed for t in range(n_dec)]
+    pre_b, dec_b = algorithmic_bytes(w, elem)
+    step_b = pre_b + n_dec * dec_b
+    attn_avg_s = sum(attn_ms) / len(attn_ms) / 1e3
+    dec_call_s = sum(dec_ms) / len(dec_ms) / 1e3 / n_dec
+    fl_alg, fl_exec = score_flops(w)
+    score_s = sum(score_ms) / len(score_ms) / 1e3
+    achieved = dec_b / attn_avg_s / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(step_b * args.steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": (f"{w['name']}: batch {B}, {Hq}q/{w['n_kv_heads']}kv heads, "
+                                f"d {w['d_qk']}, prompt {L} -> C={C} ({w['L_sink']}+{w['K']}+"
+                                f"{w['L_recent']}), W={w['W']}, pool {w['pool']}, "
+                                f"{n_dec} decode steps, {R} cache copies"),
+                   "global_batch": B, "seq_len": L, "cache_slots": C,
+                   "decode_steps_per_step": n_dec, "parallelism": "single GPU"},
+        "decode_tokens_per_s": round(B * n_dec * args.steps / wall, 1),
+        "decode_attn_GBps": round(dec_b / dec_call_s / 1e9, 1),
+        "decode_step_us": round(1e6 * dec_call_s, 2),
+        "prefill_compress_ms_per_layer": round(sum(pre_ms) / len(pre_ms), 4),
+        "roofline": {
+            "kernel": "decode_attend_kernel (split-C flash-decode)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(1e6 * attn_avg_s, 3),
+            "bytes_per_launch": dec_b,
+        },
+        "score_kernels": {
+            "avg_us": round(1e6 * score_s, 2),
+            "tflops_algorithmic": round(fl_alg / score_s / 1e12, 2),
+            "tflops_executed": round(fl_exec / score_s / 1e12, 2),
+            "frac_bf16_peak_executed": round(fl_exec / score_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
+    }
+    hip.destroy([e for p in ev_score for e in p] + [e for p in ev_attn for e in p])
+    if not args.no_cpu_baseline:
+        cpu_inp = {k: (v[:16] if v is not None else None) for k, v in inp.items()}
+        res["cpu_baseline"] = cpu_baseline(w, cpu_inp, dec)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

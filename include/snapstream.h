@@ -1,0 +1,180 @@
+/*
+ * libsnapstream: the data-parallel hot path of SnapStream (fixed-size KV cache
+ * built at prefill, ring-buffer decode over it) for AMD Instinct MI355X
+ * (gfx950).  Plain C ABI; every buffer is caller-owned.
+ *
+ * Sources, by page title and section:
+ *   "SnapStream: Efficient Long Sequence Decoding on Dataflow Accelerators",
+ *     abstract: StreamingLLM sinks/recency fused with SnapKV selection into a
+ *     fixed-size cache that works under static graphs and continuous batching.
+ *   "SnapStream: Taming KV-Cache Eviction for Dataflow Accelerators" (episode
+ *     companion), sections
+ *       "Fixed-Size Cache Layout"  - built once at prefill: sink tokens +
+ *                                    SnapKV top-K middle + recent window;
+ *                                    L_sink, K, L_recent are hyperparameters;
+ *       "Ring Buffer vs. Naive Slicing" - decode rotates only the recent
+ *                                    window: a scatter into a fixed index, no
+ *                                    gather, no concatenation;
+ *       "Why This Wasn't Already Standard" - static shapes; requests of one
+ *                                    batch at different points of their life;
+ *       "Prefill / Decode Pipeline" - decode is memory-bound on the cache;
+ *       "Infinity-Bench KV Retrieval" - pooling-based top-K selection.
+ *
+ * Conventions that the pages leave open (the library's reading):
+ *   - score of middle key i: sum over the G q-heads of its kv-head and over
+ *     the last W prompt queries of that query's causal softmax probability of
+ *     key i (softmax over every prompt key up to the query's own position);
+ *   - max-pool of odd width `pool`, stride 1, window clipped to the middle
+ *     region [L_sink, L - L_recent);
+ *   - top-K in the order (pooled score descending, position ascending); the K
+ *     kept tokens occupy slots L_sink .. L_sink+K-1 in ascending position;
+ *   - ring: position t >= L_sink+K lives in slot
+ *     L_sink + K + ((t - L_sink - K) mod L_recent); a prompt with L <= C is
+ *     stored uncompressed with token t in slot t;
+ *   - rotary embedding (rotate-half, pairs (i, i + d_rot/2) of the range
+ *     [rope_begin, rope_end), inv_freq_i = rope_theta^(-2i/d_rot)) is applied
+ *     at the token's absolute position before the key is cached; angles are
+ *     computed in fp64 and the rotated key is rounded once to the cache dtype;
+ *   - decode writes the new token first, then attends over slots
+ *     [0, min(pos + 1, C)), the new token included.
+ */
+#ifndef SNAPSTREAM_H
+#define SNAPSTREAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_INVALID_ARG = 1,  /* a scalar or pointer argument is invalid; nothing was launched */
+  SS_ERR_UNSUPPORTED = 2,  /* valid, but this build has no kernel for the shape/dtype */
+  SS_ERR_WORKSPACE = 3,    /* ws_bytes is smaller than the matching *_workspace_bytes() */
+  SS_ERR_HIP = 4           /* a HIP launch failed (hipGetLastError after the launch) */
+} ss_status;
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/* One attention layer and its fixed cache.  C = L_sink + K + L_recent slots.
+ * Supported (d_qk, d_v, dtype): (64, 64, f32|bf16), (128, 128, f32|bf16),
+ * (576, 512, bf16) with v_aliases_k = 1 (MLA absorbed latent).  G = n_q_heads /
+ * n_kv_heads must be an integer <= 16; G * W <= 256. */
+typedef struct {
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t d_qk;
+  int32_t d_v;
+  int32_t v_aliases_k;  /* 1: value = first d_v dims of the cached key (MLA) */
+  int32_t L_sink;       /* >= 0 */
+  int32_t K;            /* >= 0, top-K budget of the middle region */
+  int32_t L_recent;     /* >= 1, ring length */
+  int32_t W;            /* >= 1, observation window (last W prompt queries) */
+  int32_t pool;         /* odd, >= 1, max-pool width */
+  float scale;          /* softmax scale; 0 -> 1/sqrt(d_qk) */
+  float rope_theta;     /* 0 -> no rotary embedding at decode */
+  int32_t rope_begin;   /* rotate dims [rope_begin, rope_end) (even length) */
+  int32_t rope_end;
+  int32_t dtype;        /* ss_dtype of q/k/v, cache and out */
+} ss_config;
+
+/* The fixed-shape cache of B_max request rows; device memory, caller-owned,
+ * never resized.  Layouts (row-major):
+ *   k        [B_max, n_kv_heads, C, d_qk]
+ *   v        [B_max, n_kv_heads, C, d_v]   (NULL when v_aliases_k)
+ *   slot_pos [B_max, n_kv_heads, C] int32  absolute position held by a slot, -1 empty
+ *   n_tokens [B_max] int32                 tokens seen by the row (prompt + decoded)
+ * The valid slots of row b are [0, min(n_tokens[b], C)). */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t* slot_pos;
+  int32_t* n_tokens;
+  int32_t B_max;
+} ss_cache;
+
+/* Number of cache slots C = L_sink + K + L_recent, or -1 if cfg is invalid. */
+int32_t ss_cache_slots(const ss_config* cfg);
+
+/* Workspace (device bytes) needed by ss_prefill_compress for b requests of
+ * L prompt tokens, and by ss_decode_step for a cache of B_max rows.  0 if the
+ * arguments are invalid. */
+size_t ss_prefill_workspace_bytes(const ss_config* cfg, int32_t b, int32_t L);
+size_t ss_decode_workspace_bytes(const ss_config* cfg, int32_t B_max);
+
+/* Build the fixed cache of b requests at prefill ("Fixed-Size Cache Layout":
+ * built once at prefill; SnapKV scoring of the middle by the observation
+ * window, sinks and the recent window always kept).
+ *
+ *   q_obs  [b, n_q_heads, W, d_qk]   queries of prompt positions L-W .. L-1 (post-RoPE)
+ *   k      [b, n_kv_heads, L, d_qk]  prompt keys (post-RoPE)
+ *   v      [b, n_kv_heads, L, d_v]   prompt values (NULL when v_aliases_k)
+ *   rows   device int32 [b]: destination cache row of each request, or NULL
+ *          for rows 0 .. b-1 (continuous-batching admission into chosen rows)
+ *   raw_out    optional device float [b, n_kv_heads, m], m = L - L_sink - L_recent:
+ *              the middle-key scores (written only when L > C)
+ *   pooled_out optional device float [b, n_kv_heads, m]: the pooled scores
+ *   sel_out    optional device int32 [b, n_kv_heads, K]: kept middle tokens as
+ *              indices into the middle region, ascending
+ *   ws, ws_bytes  device workspace of >= ss_prefill_workspace_bytes(cfg, b, L)
+ *
+ * Writes, for every request i and kv-head h: cache->k/v rows of slots [0, C)
+ * (L > C) or [0, L) (L <= C), slot_pos of all C slots, n_tokens[row] = L.
+ * Requires W <= L_recent when L > C (the window lies in the recent region).
+ * Enqueued on `stream`; no host synchronisation, no allocation. */
+ss_status ss_prefill_compress(const ss_config* cfg, const void* q_obs, const void* k,
+                              const void* v, int32_t b, int32_t L, const int32_t* rows,
+                              const ss_cache* cache, float* raw_out, float* pooled_out,
+                              int32_t* sel_out, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* One decode step of every cache row ("Ring Buffer vs. Naive Slicing": write
+ * the new key/value into its fixed ring slot, evicting position pos -
+ * L_recent; then memory-bound attention over the fixed cache).
+ *
+ *   q      [B_max, n_q_heads, d_qk]   pre-RoPE query of the new token
+ *   k_new  [B_max, n_kv_heads, d_qk]  pre-RoPE key of the new token
+ *   v_new  [B_max, n_kv_heads, d_v]   value of the new token (NULL when v_aliases_k)
+ *   pos    device int32 [B_max]: absolute position of the new token; < 0 marks
+ *          an inactive row (no state change, out row = 0)
+ *   out    [B_max, n_q_heads, d_v]    attention output, cache dtype
+ *   err_flag  optional device int32: set to 1 when an active row has
+ *          pos != n_tokens (the step is still applied at pos); never cleared
+ *   ws, ws_bytes  device workspace of >= ss_decode_workspace_bytes(cfg, B_max)
+ *
+ * Enqueued on `stream`; no host synchronisation, no allocation. */
+ss_status ss_decode_step(const ss_config* cfg, const void* q, const void* k_new,
+                         const void* v_new, const int32_t* pos, const ss_cache* cache,
+                         void* out, int32_t* err_flag, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Profiling variants: identical to the calls above, and additionally record
+ * `begin` / `end` on `stream` immediately before and after the dominant
+ * kernels - the split-C attention kernel of ss_decode_step, the two score
+ * passes (row statistics through column scores) of ss_prefill_compress.
+ * Either event may be NULL.  The events are caller-created (hipEventCreate);
+ * the caller reads hipEventElapsedTime after its own synchronisation.  When a
+ * prompt is stored uncompressed (L <= C) no score kernel runs and the two
+ * events are recorded back to back. */
+ss_status ss_prefill_compress_timed(const ss_config* cfg, const void* q_obs, const void* k,
+                                    const void* v, int32_t b, int32_t L, const int32_t* rows,
+                                    const ss_cache* cache, float* raw_out, float* pooled_out,
+                                    int32_t* sel_out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream, hipEvent_t begin, hipEvent_t end);
+ss_status ss_decode_step_timed(const ss_config* cfg, const void* q, const void* k_new,
+                               const void* v_new, const int32_t* pos, const ss_cache* cache,
+                               void* out, int32_t* err_flag, void* ws, size_t ws_bytes,
+                               hipStream_t stream, hipEvent_t begin, hipEvent_t end);
+
+/* Static description of a status code. */
+const char* ss_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNAPSTREAM_H */

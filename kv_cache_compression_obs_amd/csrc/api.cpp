@@ -1,0 +1,305 @@
+// C ABI of libsnapstream: argument checks, workspace carving and kernel
+// launches.  No allocation, no host synchronisation, no global state.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/snapstream.h"
+#include "launch.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool supported_shape(const ss_config* c) {
+  if (c->v_aliases_k) return false;  // the latent (MLA) kernels are not in this build yet
+  if (c->dtype != SS_F32 && c->dtype != SS_BF16) return false;
+  return (c->d_qk == 64 && c->d_v == 64) || (c->d_qk == 128 && c->d_v == 128);
+}
+
+// Structural validity of a configuration (independent of the call).
+ss_status check_config(const ss_config* c) {
+  if (c == nullptr) return SS_ERR_INVALID_ARG;
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads != 0)
+    return SS_ERR_INVALID_ARG;
+  if (c->d_qk < 1 || c->d_v < 1) return SS_ERR_INVALID_ARG;
+  if (c->v_aliases_k && c->d_v > c->d_qk) return SS_ERR_INVALID_ARG;
+  if (c->L_sink < 0 || c->K < 0 || c->L_recent < 1 || c->W < 1) return SS_ERR_INVALID_ARG;
+  if (c->pool < 1 || c->pool % 2 == 0) return SS_ERR_INVALID_ARG;
+  if (!(c->scale >= 0.f) || !isfinite(c->scale)) return SS_ERR_INVALID_ARG;
+  if (!(c->rope_theta >= 0.f) || !isfinite(c->rope_theta)) return SS_ERR_INVALID_ARG;
+  if (c->rope_theta > 0.f) {
+    if (c->rope_begin < 0 || c->rope_end > c->d_qk || c->rope_end <= c->rope_begin ||
+        (c->rope_end - c->rope_begin) % 2 != 0)
+      return SS_ERR_INVALID_ARG;
+  }
+  const long long C = static_cast<long long>(c->L_sink) + c->K + c->L_recent;
+  if (C > (1LL << 30)) return SS_ERR_INVALID_ARG;
+  if (c->dtype != SS_F32 && c->dtype != SS_BF16) return SS_ERR_INVALID_ARG;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (!supported_shape(c) || G > 16 || G * c->W > 128) return SS_ERR_UNSUPPORTED;
+  return SS_OK;
+}
+
+int cache_slots(const ss_config* c) { return c->L_sink + c->K + c->L_recent; }
+float scale_log2(const ss_config* c) {
+  const float s = c->scale > 0.f ? c->scale : 1.0f / sqrtf(static_cast<float>(c->d_qk));
+  return s * 1.4426950408889634f;
+}
+
+// ---------------------------------------------------------------- prefill
+struct PrefillPlan {
+  bool compressed;
+  int m, Rg, chunk1, n_chunk1, chunk2, n_chunk2;
+  size_t off_part1, off_rowstat, off_raw, off_pooled, off_sel, total;
+};
+
+PrefillPlan plan_prefill(const ss_config* c, int b, int L) {
+  PrefillPlan p{};
+  const int C = cache_slots(c);
+  p.compressed = L > C;
+  if (!p.compressed) return p;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  p.m = L - c->L_sink - c->L_recent;
+  p.Rg = (G * c->W + 15) / 16 * 16;
+  p.chunk1 = 2048;
+  p.n_chunk1 = (L + p.chunk1 - 1) / p.chunk1;
+  p.chunk2 = 1024;
+  p.n_chunk2 = (p.m + p.chunk2 - 1) / p.chunk2;
+  const size_t groups = static_cast<size_t>(b) * c->n_kv_heads;
+  size_t off = 0;
+  p.off_part1 = off;
+  off += align_up(groups * p.Rg * p.n_chunk1 * 2 * sizeof(float));
+  p.off_rowstat = off;
+  off += align_up(groups * p.Rg * 2 * sizeof(float));
+  p.off_raw = off;
+  off += align_up(groups * p.m * sizeof(float));
+  p.off_pooled = off;
+  off += align_up(groups * p.m * sizeof(float));
+  p.off_sel = off;
+  off += align_up(groups * (c->K > 0 ? c->K : 1) * sizeof(int32_t));
+  p.total = off;
+  return p;
+}
+
+// ----------------------------------------------------------------- decode
+struct DecodePlan {
+  int split, n_split;
+  size_t off_q, off_o, off_ml, total;
+};
+
+DecodePlan plan_decode(const ss_config* c, int B_max) {
+  DecodePlan p{};
+  const int C = cache_slots(c);
+  const long long groups = static_cast<long long>(B_max) * c->n_kv_heads;
+  // Split the C slots so that the grid holds about 2048 workgroups (8 per CU
+  // on 256 CUs) when every slot is valid; at least one 32-slot tile each.
+  int tiles = (C + ss::DECODE_TILE - 1) / ss::DECODE_TILE;
+  long long want = (2048 + groups - 1) / groups;
+  if (want < 1) want = 1;
+  int tiles_per_split = static_cast<int>((tiles + want - 1) / want);
+  if (tiles_per_split < 1) tiles_per_split = 1;
+  p.split = tiles_per_split * ss::DECODE_TILE;
+  p.n_split = (C + p.split - 1) / p.split;
+  const size_t rows_q = static_cast<size_t>(B_max) * c->n_q_heads;
+  size_t off = 0;
+  p.off_q = off;
+  off += align_up(rows_q * c->d_qk * sizeof(float));
+  p.off_o = off;
+  off += align_up(rows_q * p.n_split * c->d_v * sizeof(float));
+  p.off_ml = off;
+  off += align_up(rows_q * p.n_split * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ss_cache_slots(const ss_config* cfg) {
+  const ss_status s = check_config(cfg);
+  if (s == SS_ERR_INVALID_ARG) return -1;
+  return cache_slots(cfg);
+}
+
+size_t ss_prefill_workspace_bytes(const ss_config* cfg, int32_t b, int32_t L) {
+  if (check_config(cfg) != SS_OK || b < 1 || L < 1) return 0;
+  const PrefillPlan p = plan_prefill(cfg, b, L);
+  return p.compressed ? p.total : ALIGN;  // a non-zero size keeps the pointer rule uniform
+}
+
+size_t ss_decode_workspace_bytes(const ss_config* cfg, int32_t B_max) {
+  if (check_config(cfg) != SS_OK || B_max < 1) return 0;
+  return plan_decode(cfg, B_max).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, const void* v,
+                       int32_t b, int32_t L, const int32_t* rows, const ss_cache* cache,
+                       float* raw_out, float* pooled_out, int32_t* sel_out, void* ws,
+                       size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const ss_status cs = check_config(cfg);
+  if (cs != SS_OK) return cs;
+  if (cache == nullptr || b < 1 || L < 1 || k == nullptr || cache->k == nullptr ||
+      cache->slot_pos == nullptr || cache->n_tokens == nullptr || cache->B_max < 1)
+    return SS_ERR_INVALID_ARG;
+  if (!cfg->v_aliases_k && (v == nullptr || cache->v == nullptr)) return SS_ERR_INVALID_ARG;
+  if (rows == nullptr && b > cache->B_max) return SS_ERR_INVALID_ARG;
+  const int C = cache_slots(cfg);
+  const bool compressed = L > C;
+  if (compressed) {
+    if (q_obs == nullptr) return SS_ERR_INVALID_ARG;
+    if (cfg->W > L || cfg->W > cfg->L_recent) return SS_ERR_INVALID_ARG;
+  }
+  const PrefillPlan p = plan_prefill(cfg, b, L);
+  if (ws == nullptr || ws_bytes < (compressed ? p.total : ALIGN)) return SS_ERR_WORKSPACE;
+
+  ss::PrefillArgs a{};
+  a.q_obs = q_obs;
+  a.k = k;
+  a.v = cfg->v_aliases_k ? nullptr : v;
+  a.rows = rows;
+  a.kc = cache->k;
+  a.vc = cfg->v_aliases_k ? nullptr : cache->v;
+  a.slot_pos = cache->slot_pos;
+  a.n_tokens = cache->n_tokens;
+  a.b = b;
+  a.B_max = cache->B_max;
+  a.L = L;
+  a.Hq = cfg->n_q_heads;
+  a.Hkv = cfg->n_kv_heads;
+  a.G = cfg->n_q_heads / cfg->n_kv_heads;
+  a.W = cfg->W;
+  a.C = C;
+  a.S = cfg->L_sink;
+  a.K = cfg->K;
+  a.R = cfg->L_recent;
+  a.pool = cfg->pool;
+  a.scale_log2 = scale_log2(cfg);
+  if (compressed) {
+    char* w = static_cast<char*>(ws);
+    a.m = p.m;
+    a.Rg = p.Rg;
+    a.chunk1 = p.chunk1;
+    a.n_chunk1 = p.n_chunk1;
+    a.chunk2 = p.chunk2;
+    a.n_chunk2 = p.n_chunk2;
+    a.part1 = reinterpret_cast<float*>(w + p.off_part1);
+    a.rowstat = reinterpret_cast<float*>(w + p.off_rowstat);
+    a.raw = raw_out ? raw_out : reinterpret_cast<float*>(w + p.off_raw);
+    a.pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(w + p.off_pooled);
+    a.sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + p.off_sel);
+    if (ss::launch_prefill_scores(cfg->dtype, cfg->d_qk, a, stream, ev0, ev1) != hipSuccess)
+      return SS_ERR_HIP;
+    if (ss::launch_prefill_select(a, stream) != hipSuccess) return SS_ERR_HIP;
+  } else {
+    if (ev0 != nullptr && hipEventRecord(ev0, stream) != hipSuccess) return SS_ERR_HIP;
+    if (ev1 != nullptr && hipEventRecord(ev1, stream) != hipSuccess) return SS_ERR_HIP;
+  }
+  if (ss::launch_prefill_gather(cfg->dtype, cfg->d_qk, cfg->d_v, cfg->v_aliases_k, compressed, a,
+                                stream) != hipSuccess)
+    return SS_ERR_HIP;
+  return SS_OK;
+}
+
+ss_status decode_impl(const ss_config* cfg, const void* q, const void* k_new, const void* v_new,
+                      const int32_t* pos, const ss_cache* cache, void* out, int32_t* err_flag,
+                      void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t ev0,
+                      hipEvent_t ev1) {
+  const ss_status cs = check_config(cfg);
+  if (cs != SS_OK) return cs;
+  if (cache == nullptr || q == nullptr || k_new == nullptr || pos == nullptr || out == nullptr ||
+      cache->k == nullptr || cache->slot_pos == nullptr || cache->n_tokens == nullptr ||
+      cache->B_max < 1)
+    return SS_ERR_INVALID_ARG;
+  if (!cfg->v_aliases_k && (v_new == nullptr || cache->v == nullptr)) return SS_ERR_INVALID_ARG;
+  const DecodePlan p = plan_decode(cfg, cache->B_max);
+  if (ws == nullptr || ws_bytes < p.total) return SS_ERR_WORKSPACE;
+
+  ss::DecodeArgs a{};
+  char* w = static_cast<char*>(ws);
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = cfg->v_aliases_k ? nullptr : v_new;
+  a.pos = pos;
+  a.kc = cache->k;
+  a.vc = cfg->v_aliases_k ? nullptr : cache->v;
+  a.slot_pos = cache->slot_pos;
+  a.n_tokens = cache->n_tokens;
+  a.out = out;
+  a.err = err_flag;
+  a.q_rot = reinterpret_cast<float*>(w + p.off_q);
+  a.part_o = reinterpret_cast<float*>(w + p.off_o);
+  a.part_ml = reinterpret_cast<float*>(w + p.off_ml);
+  a.B = cache->B_max;
+  a.Hq = cfg->n_q_heads;
+  a.Hkv = cfg->n_kv_heads;
+  a.G = cfg->n_q_heads / cfg->n_kv_heads;
+  a.C = cache_slots(cfg);
+  a.S = cfg->L_sink;
+  a.K = cfg->K;
+  a.R = cfg->L_recent;
+  a.split = p.split;
+  a.n_split = p.n_split;
+  a.scale_log2 = scale_log2(cfg);
+  a.rope_theta = cfg->rope_theta;
+  a.rope_begin = cfg->rope_begin;
+  a.rope_end = cfg->rope_end;
+  if (ss::launch_decode(cfg->dtype, cfg->d_qk, cfg->d_v, cfg->v_aliases_k, a, stream, ev0, ev1) !=
+      hipSuccess)
+    return SS_ERR_HIP;
+  return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_prefill_compress(const ss_config* cfg, const void* q_obs, const void* k,
+                              const void* v, int32_t b, int32_t L, const int32_t* rows,
+                              const ss_cache* cache, float* raw_out, float* pooled_out,
+                              int32_t* sel_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return prefill_impl(cfg, q_obs, k, v, b, L, rows, cache, raw_out, pooled_out, sel_out, ws,
+                      ws_bytes, stream, nullptr, nullptr);
+}
+
+ss_status ss_prefill_compress_timed(const ss_config* cfg, const void* q_obs, const void* k,
+                                    const void* v, int32_t b, int32_t L, const int32_t* rows,
+                                    const ss_cache* cache, float* raw_out, float* pooled_out,
+                                    int32_t* sel_out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream, hipEvent_t begin, hipEvent_t end) {
+  return prefill_impl(cfg, q_obs, k, v, b, L, rows, cache, raw_out, pooled_out, sel_out, ws,
+                      ws_bytes, stream, begin, end);
+}
+
+ss_status ss_decode_step(const ss_config* cfg, const void* q, const void* k_new,
+                         const void* v_new, const int32_t* pos, const ss_cache* cache, void* out,
+                         int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(cfg, q, k_new, v_new, pos, cache, out, err_flag, ws, ws_bytes, stream,
+                     nullptr, nullptr);
+}
+
+ss_status ss_decode_step_timed(const ss_config* cfg, const void* q, const void* k_new,
+                               const void* v_new, const int32_t* pos, const ss_cache* cache,
+                               void* out, int32_t* err_flag, void* ws, size_t ws_bytes,
+                               hipStream_t stream, hipEvent_t begin, hipEvent_t end) {
+  return decode_impl(cfg, q, k_new, v_new, pos, cache, out, err_flag, ws, ws_bytes, stream, begin,
+                     end);
+}
+
+const char* ss_status_string(int32_t status) {
+  switch (status) {
+    case SS_OK: return "ok";
+    case SS_ERR_INVALID_ARG: return "invalid argument";
+    case SS_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SS_ERR_WORKSPACE: return "workspace too small";
+    case SS_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

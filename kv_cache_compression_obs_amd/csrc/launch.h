@@ -1,0 +1,65 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+struct DecodeArgs {
+  const void* q;         // [B, Hq, D] pre-RoPE
+  const void* k_new;     // [B, Hkv, D] pre-RoPE
+  const void* v_new;     // [B, Hkv, DV] or null (aliased)
+  const int32_t* pos;    // [B]
+  void* kc;              // cache k [B, Hkv, C, D]
+  void* vc;              // cache v [B, Hkv, C, DV] or null (aliased)
+  int32_t* slot_pos;     // [B, Hkv, C]
+  int32_t* n_tokens;     // [B]
+  void* out;             // [B, Hq, DV]
+  int32_t* err;          // optional
+  float* q_rot;          // ws: rotated queries [B, Hq, D], fp32
+  float* part_o;         // ws: [B, Hq, n_split, DV] unnormalised partial outputs
+  float* part_ml;        // ws: [B, Hq, n_split, 2] (running max in log2 units, sum)
+  int B, Hq, Hkv, G, C, S, K, R;
+  int split, n_split;    // slots per split (multiple of 32), number of splits
+  float scale_log2;      // softmax scale * log2(e)
+  double rope_theta;     // 0: no rotation
+  int rope_begin, rope_end;
+};
+
+struct PrefillArgs {
+  const void* q_obs;     // [b, Hq, W, D]
+  const void* k;         // [b, Hkv, L, D]
+  const void* v;         // [b, Hkv, L, DV] or null (aliased)
+  const int32_t* rows;   // [b] destination rows or null
+  void* kc;              // cache k [B_max, Hkv, C, D]
+  void* vc;              // cache v or null
+  int32_t* slot_pos;
+  int32_t* n_tokens;
+  float* part1;          // ws: [b, Hkv, Rg, n_chunk1, 2] per-chunk (max, sum)
+  float* rowstat;        // ws: [b, Hkv, Rg, 2] (max, 1/sum)
+  float* raw;            // [b, Hkv, m]
+  float* pooled;         // [b, Hkv, m]
+  int32_t* sel;          // [b, Hkv, K]
+  int b, B_max, L, Hq, Hkv, G, W, C, S, K, R, pool, m;
+  int Rg;                // rows per group padded to a multiple of 16
+  int chunk1, n_chunk1;  // keys per row-stat workgroup, count
+  int chunk2, n_chunk2;  // middle keys per column-score workgroup, count
+  float scale_log2;
+};
+
+// Returns hipErrorInvalidValue when no kernel exists for (dtype, D, DV).
+// ev0/ev1 (nullable) are recorded right before/after the dominant kernels.
+hipError_t launch_decode(int dtype, int D, int DV, int alias, const DecodeArgs& a,
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStream_t st,
+                                 hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_gather(int dtype, int D, int DV, int alias, bool compressed,
+                                 const PrefillArgs& a, hipStream_t st);
+
+// Tiling constants the host uses to size workspaces.
+constexpr int DECODE_TILE = 32;   // slots per decode tile
+constexpr int SCORE_KT_MAX = 64;  // keys per score tile (chunks are multiples of it)
+
+}  // namespace ss

@@ -1,0 +1,365 @@
+// Prefill-time compression: observation-window scoring of the prompt keys
+// and the gather that builds the fixed-size cache.
+//
+// "SnapStream: Taming KV-Cache Eviction for Dataflow Accelerators", sections
+// "Two Ingredients, Fused" (SnapKV attention-based selection fused with
+// StreamingLLM sinks + window) and "Fixed-Size Cache Layout" (built once at
+// prefill: sinks + top-K middle + recent window).
+//
+// Score of middle key i = sum over the G q-heads of the kv-head and the W
+// observation queries of that query's causal softmax probability of key i.
+// Two passes over the keys, both a dense Q_obs . K^T contraction on MFMA:
+//   pass 1 (score_rowstat): per query row, running max and sum of 2^x over
+//            key chunks, x = scale*log2(e) * q.k; combined in fp64 across
+//            chunks (score_rowstat_combine) into (max M, weight w = 1/sum);
+//   pass 2 (score_columns): over the middle keys only, recompute x and sum
+//            2^(x - M) * w over the rows of the group, per key.
+// Both passes compute x with the same instruction sequence, so pass 2 sees
+// bit-identical logits to the ones pass 1 normalised.
+#include "common.h"
+#include "launch.h"
+
+namespace ss {
+
+namespace {
+
+constexpr int SW = 8;          // waves per score workgroup (one 16-row block each)
+constexpr int SNT = SW * 64;   // threads per score workgroup
+
+template <typename T, int D, int KT>
+struct KeyTile {
+  static constexpr int ES = static_cast<int>(sizeof(T));
+  static constexpr int KROW = D * ES;      // bytes of one key row
+  static constexpr int LROW = KROW + 16;   // LDS row stride (bytes)
+  static constexpr int KCH = KROW / 16;    // 16-byte chunks per row
+  static constexpr int NLD = KT * KCH / SNT;
+  static constexpr int BYTES = KT * LROW;
+  static_assert((KT * KCH) % SNT == 0, "tile must split evenly over the workgroup");
+
+  // rows t0 .. t0+KT-1 of kbase (clamped to kend-1) into registers
+  static __device__ __forceinline__ void load(uint4 (&r)[NLD], const T* kbase, int t0, int kend,
+                                              int tid) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int id = i * SNT + tid;
+      const int key = min(t0 + id / KCH, kend - 1);
+      r[i] = *reinterpret_cast<const uint4*>(
+          reinterpret_cast<const char*>(kbase + static_cast<size_t>(key) * D) + (id % KCH) * 16);
+    }
+  }
+  static __device__ __forceinline__ void store(char* buf, const uint4 (&r)[NLD], int tid) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int id = i * SNT + tid;
+      *reinterpret_cast<uint4*>(buf + (id / KCH) * LROW + (id % KCH) * 16) = r[i];
+    }
+  }
+  // B operand (K^T) fragment: lane (col, qg) takes key 16*kb + col, dims
+  // c*KSTEP + qg*KPL ..
+  static __device__ __forceinline__ typename Mma<T>::frag bfrag(const char* buf, int kb, int c,
+                                                                int col, int qg) {
+    return Mma<T>::load(reinterpret_cast<const T*>(
+        buf + (16 * kb + col) * LROW + (c * Mma<T>::KSTEP + qg * Mma<T>::KPL) * ES));
+  }
+};
+
+// Q_obs rows of the group (G heads x W rows, contiguous) as A fragments.
+template <typename T, int D>
+__device__ __forceinline__ void load_q(typename Mma<T>::frag (&qf)[D / Mma<T>::KSTEP],
+                                       const PrefillArgs& a, int bi, int h, int row, int qg) {
+  const T* qbase = static_cast<const T*>(a.q_obs) +
+                   (static_cast<size_t>(bi) * a.Hq + static_cast<size_t>(h) * a.G) * a.W * D;
+  const bool ok = row < a.G * a.W;
+#pragma unroll
+  for (int c = 0; c < D / Mma<T>::KSTEP; ++c)
+    qf[c] = ok ? Mma<T>::load(qbase + static_cast<size_t>(row) * D + c * Mma<T>::KSTEP +
+                              qg * Mma<T>::KPL)
+               : Mma<T>::zero();
+}
+
+// Pass 1.  Grid (n_chunk1, Hkv, b).  Wave w owns rows 16w .. 16w+15 of the
+// group; accumulator lane (col, qg) register r holds row 16w + 4qg + r and key
+// 16kb + col of the tile.  Each lane keeps running (max, sum) of its rows
+// over the keys it sees; the 16 lanes of a row are merged at the end.
+template <typename T, int D, int KT>
+__global__ __launch_bounds__(SNT) void score_rowstat_kernel(PrefillArgs a) {
+  using MM = Mma<T>;
+  using KTile = KeyTile<T, D, KT>;
+  constexpr int NC = D / MM::KSTEP;
+  constexpr int NKB = KT / 16;
+  __shared__ __attribute__((aligned(16))) char lds[2 * KTile::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, qg = lane >> 4;
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const bool active = 16 * wave < a.G * a.W;  // wave-uniform
+
+  typename MM::frag qf[NC];
+  load_q<T, D>(qf, a, bi, h, 16 * wave + col, qg);
+  int lim[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 16 * wave + 4 * qg + r;
+    lim[r] = row < a.G * a.W ? a.L - a.W + row % a.W : -1;  // last visible key
+  }
+  const int k0 = chunk * a.chunk1, k1 = min(k0 + a.chunk1, a.L);
+  const T* kbase = static_cast<const T*>(a.k) + (static_cast<size_t>(bi) * a.Hkv + h) * a.L * D;
+
+  float m[4], s[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    s[r] = 0.f;
+  }
+  uint4 ld[KTile::NLD];
+  KTile::load(ld, kbase, k0, k1, tid);
+  KTile::store(lds, ld, tid);
+  __syncthreads();
+  int t = 0;
+  for (int t0 = k0; t0 < k1; t0 += KT, ++t) {
+    const char* cur = lds + (t & 1) * KTile::BYTES;
+    const bool more = t0 + KT < k1;
+    if (more) KTile::load(ld, kbase, t0 + KT, k1, tid);
+    if (active) {
+      float x[NKB][4];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc = MM::mma(qf[c], KTile::bfrag(cur, kb, c, col, qg), acc);
+        const int key = t0 + 16 * kb + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[kb][r] = (key < k1 && key <= lim[r]) ? acc[r] * a.scale_log2 : -INFINITY;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float tm = x[0][r];
+#pragma unroll
+        for (int kb = 1; kb < NKB; ++kb) tm = fmaxf(tm, x[kb][r]);
+        const float mn = fmaxf(m[r], tm);
+        if (mn != -INFINITY) {
+          float add = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) add += exp2f(x[kb][r] - mn);
+          s[r] = s[r] * exp2f(m[r] - mn) + add;
+          m[r] = mn;
+        }
+      }
+    }
+    if (more) KTile::store(lds + ((t + 1) & 1) * KTile::BYTES, ld, tid);
+    __syncthreads();
+  }
+  if (!active) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float M = m[r];
+    M = xor_max(M, 1);
+    M = xor_max(M, 2);
+    M = xor_max(M, 4);
+    M = xor_max(M, 8);
+    float sv = m[r] == -INFINITY ? 0.f : s[r] * exp2f(m[r] - M);
+    sv = xor_sum(sv, 1);
+    sv = xor_sum(sv, 2);
+    sv = xor_sum(sv, 4);
+    sv = xor_sum(sv, 8);
+    const int row = 16 * wave + 4 * qg + r;
+    if (col == 0 && row < a.Rg) {
+      const size_t idx = ((static_cast<size_t>(bi) * a.Hkv + h) * a.Rg + row) * a.n_chunk1 + chunk;
+      a.part1[2 * idx] = M;
+      a.part1[2 * idx + 1] = sv;
+    }
+  }
+}
+
+// Merge the per-chunk (max, sum) of every query row in fp64.
+__global__ __launch_bounds__(256) void score_rowstat_combine_kernel(PrefillArgs a) {
+  const size_t n = static_cast<size_t>(a.b) * a.Hkv * a.Rg;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const float* p = a.part1 + 2 * idx * a.n_chunk1;
+  float M = -INFINITY;
+  for (int c = 0; c < a.n_chunk1; ++c) M = fmaxf(M, p[2 * c]);
+  double S = 0.0;
+  if (M != -INFINITY)
+    for (int c = 0; c < a.n_chunk1; ++c)
+      if (p[2 * c] != -INFINITY)
+        S += static_cast<double>(p[2 * c + 1]) * exp2(static_cast<double>(p[2 * c]) - M);
+  a.rowstat[2 * idx] = M;
+  a.rowstat[2 * idx + 1] = S > 0.0 ? static_cast<float>(1.0 / S) : 0.f;
+}
+
+// Pass 2.  Grid (n_chunk2, Hkv, b) over the middle keys [S, L-R).  Every
+// middle key is visible to every observation row (the window lies inside the
+// recent region), so no causal mask.  Column sums: 4 rows in registers, then
+// the 4 lane groups (xor 16, 32), then the 8 waves through LDS in wave order.
+template <typename T, int D, int KT>
+__global__ __launch_bounds__(SNT) void score_columns_kernel(PrefillArgs a) {
+  using MM = Mma<T>;
+  using KTile = KeyTile<T, D, KT>;
+  constexpr int NC = D / MM::KSTEP;
+  constexpr int NKB = KT / 16;
+  __shared__ __attribute__((aligned(16))) char lds[2 * KTile::BYTES];
+  __shared__ float red[2][SW][KT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, qg = lane >> 4;
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int nrb = cdiv(a.G * a.W, 16);
+  const bool active = wave < nrb;
+
+  typename MM::frag qf[NC];
+  load_q<T, D>(qf, a, bi, h, 16 * wave + col, qg);
+  float M[4], w[4];
+  bool ok[4];
+  const size_t gidx = static_cast<size_t>(bi) * a.Hkv + h;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 16 * wave + 4 * qg + r;
+    ok[r] = row < a.G * a.W;
+    M[r] = ok[r] ? a.rowstat[2 * (gidx * a.Rg + row)] : 0.f;
+    w[r] = ok[r] ? a.rowstat[2 * (gidx * a.Rg + row) + 1] : 0.f;
+  }
+  const int mend = a.L - a.R;
+  const int k0 = a.S + chunk * a.chunk2, k1 = min(k0 + a.chunk2, mend);
+  const T* kbase = static_cast<const T*>(a.k) + gidx * a.L * D;
+  float* raw = a.raw + gidx * a.m - a.S;  // indexed by absolute key
+
+  uint4 ld[KTile::NLD];
+  KTile::load(ld, kbase, k0, k1, tid);
+  KTile::store(lds, ld, tid);
+  __syncthreads();
+  int t = 0;
+  for (int t0 = k0; t0 < k1; t0 += KT, ++t) {
+    const char* cur = lds + (t & 1) * KTile::BYTES;
+    const bool more = t0 + KT < k1;
+    if (more) KTile::load(ld, kbase, t0 + KT, k1, tid);
+    if (active) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc = MM::mma(qf[c], KTile::bfrag(cur, kb, c, col, qg), acc);
+        float cs = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          cs += ok[r] ? exp2f(acc[r] * a.scale_log2 - M[r]) * w[r] : 0.f;
+        cs = xor_sum(cs, 16);
+        cs = xor_sum(cs, 32);
+        if (qg == 0) red[t & 1][wave][16 * kb + col] = cs;
+      }
+    }
+    if (more) KTile::store(lds + ((t + 1) & 1) * KTile::BYTES, ld, tid);
+    __syncthreads();
+    if (tid < KT && t0 + tid < k1) {
+      float v = 0.f;
+      for (int wv = 0; wv < nrb; ++wv) v += red[t & 1][wv][tid];
+      raw[t0 + tid] = v;
+    }
+  }
+}
+
+// Build the cache rows of one request: slots [0, S) <- tokens 0..S-1, slots
+// [S, S+K) <- the selected middle tokens (ascending), ring slots <- the last R
+// tokens at S+K + ((t-S-K) mod R).  Uncompressed prompts (L <= C) map token t
+// to slot t.  Grid (cdiv(C, 16), Hkv, b); copies are 16-byte coalesced.
+// A destination row outside [0, B_max) is skipped.
+template <typename T, int D, int DV, bool ALIAS>
+__global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compressed) {
+  constexpr int SLOTS = 16;
+  constexpr int KCH = D * static_cast<int>(sizeof(T)) / 16;
+  constexpr int VCH = DV * static_cast<int>(sizeof(T)) / 16;
+  __shared__ int tok[SLOTS];
+  const int tid = threadIdx.x;
+  const int sb = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int row = a.rows ? a.rows[bi] : bi;
+  if (row < 0 || row >= a.B_max) return;  // rows outside the cache are ignored
+  const size_t gsrc = static_cast<size_t>(bi) * a.Hkv + h;
+  const size_t gdst = static_cast<size_t>(row) * a.Hkv + h;
+  if (tid < SLOTS) {
+    const int s = sb * SLOTS + tid;
+    int t = -1;
+    if (s < a.C) {
+      if (!compressed) {
+        t = s < a.L ? s : -1;
+      } else if (s < a.S) {
+        t = s;
+      } else if (s < a.S + a.K) {
+        const int j = a.sel[gsrc * a.K + (s - a.S)];
+        t = (j >= 0 && j < a.m) ? a.S + j : -1;
+      } else {
+        int r = (s - a.L) % a.R;
+        if (r < 0) r += a.R;
+        t = a.L - a.R + r;
+      }
+      a.slot_pos[gdst * a.C + s] = t;
+    }
+    tok[tid] = t;
+  }
+  if (sb == 0 && h == 0 && tid == 0) a.n_tokens[row] = a.L;
+  __syncthreads();
+  const char* ksrc = reinterpret_cast<const char*>(static_cast<const T*>(a.k) + gsrc * a.L * D);
+  char* kdst = reinterpret_cast<char*>(static_cast<T*>(a.kc) + gdst * a.C * D);
+  for (int id = tid; id < SLOTS * KCH; id += blockDim.x) {
+    const int j = id / KCH, ch = id % KCH;
+    const int t = tok[j];
+    if (t < 0) continue;
+    const size_t s = static_cast<size_t>(sb) * SLOTS + j;
+    *reinterpret_cast<uint4*>(kdst + s * KCH * 16 + ch * 16) =
+        *reinterpret_cast<const uint4*>(ksrc + static_cast<size_t>(t) * KCH * 16 + ch * 16);
+  }
+  if (ALIAS) return;
+  const char* vsrc = reinterpret_cast<const char*>(static_cast<const T*>(a.v) + gsrc * a.L * DV);
+  char* vdst = reinterpret_cast<char*>(static_cast<T*>(a.vc) + gdst * a.C * DV);
+  for (int id = tid; id < SLOTS * VCH; id += blockDim.x) {
+    const int j = id / VCH, ch = id % VCH;
+    const int t = tok[j];
+    if (t < 0) continue;
+    const size_t s = static_cast<size_t>(sb) * SLOTS + j;
+    *reinterpret_cast<uint4*>(vdst + s * VCH * 16 + ch * 16) =
+        *reinterpret_cast<const uint4*>(vsrc + static_cast<size_t>(t) * VCH * 16 + ch * 16);
+  }
+}
+
+template <typename T, int D, int KT>
+hipError_t run_scores(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
+  score_rowstat_kernel<T, D, KT><<<dim3(a.n_chunk1, a.Hkv, a.b), SNT, 0, st>>>(a);
+  const size_t rows = static_cast<size_t>(a.b) * a.Hkv * a.Rg;
+  score_rowstat_combine_kernel<<<static_cast<unsigned>(cdiv(static_cast<int>(rows), 256)), 256, 0,
+                                 st>>>(a);
+  score_columns_kernel<T, D, KT><<<dim3(a.n_chunk2, a.Hkv, a.b), SNT, 0, st>>>(a);
+  if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DV, bool ALIAS>
+hipError_t run_gather(bool compressed, const PrefillArgs& a, hipStream_t st) {
+  gather_kernel<T, D, DV, ALIAS><<<dim3(cdiv(a.C, 16), a.Hkv, a.b), 256, 0, st>>>(a, compressed);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStream_t st,
+                                 hipEvent_t ev0, hipEvent_t ev1) {
+  if (dtype == 0 && D == 64) return run_scores<float, 64, 64>(a, st, ev0, ev1);
+  if (dtype == 0 && D == 128) return run_scores<float, 128, 64>(a, st, ev0, ev1);
+  if (dtype == 1 && D == 64) return run_scores<bf16_t, 64, 64>(a, st, ev0, ev1);
+  if (dtype == 1 && D == 128) return run_scores<bf16_t, 128, 64>(a, st, ev0, ev1);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_gather(int dtype, int D, int DV, int alias, bool compressed,
+                                 const PrefillArgs& a, hipStream_t st) {
+  if (alias) return hipErrorInvalidValue;
+  if (dtype == 0 && D == 64 && DV == 64) return run_gather<float, 64, 64, false>(compressed, a, st);
+  if (dtype == 0 && D == 128 && DV == 128)
+    return run_gather<float, 128, 128, false>(compressed, a, st);
+  if (dtype == 1 && D == 64 && DV == 64) return run_gather<bf16_t, 64, 64, false>(compressed, a, st);
+  if (dtype == 1 && D == 128 && DV == 128)
+    return run_gather<bf16_t, 128, 128, false>(compressed, a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ss

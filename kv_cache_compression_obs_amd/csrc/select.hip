@@ -1,0 +1,177 @@
+// Max-pool of the middle-key scores and top-K selection per (request,
+// kv-head): "SnapStream: Taming KV-Cache Eviction for Dataflow Accelerators",
+// sections "Fixed-Size Cache Layout" (the SnapKV top-K middle segment) and
+// "Infinity-Bench KV Retrieval" (pooling-based top-K selection).
+//
+// pooled[i] = max raw[u] over the middle region, |u - i| <= (pool-1)/2.
+// The kept set is the first K of the order (pooled descending, index
+// ascending), written in ascending index order.
+//
+// One 1024-thread workgroup per group.  Scores are non-negative floats, so
+// their bit patterns order like the values.  A 3-pass radix select
+// (11 + 11 + 10 bits, LDS histograms) finds the K-th largest value T and how
+// many of the keys equal to T are kept (the lowest-indexed ones); an ordered
+// compaction (ballot + popcount per wave, wave order across the group) then
+// writes the kept indices ascending.  Integer work only after the pooling
+// max, so the result is exact for the given scores.
+#include "common.h"
+#include "launch.h"
+
+namespace ss {
+
+namespace {
+
+constexpr int NT = 1024;
+constexpr int NW = NT / 64;
+
+// Inclusive prefix sum over the 1024 threads of the workgroup.
+__device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t n = __shfl_up(v, off, 64);
+    if (lane >= off) v += n;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t w = lane < NW ? wsum[lane] : 0u;
+#pragma unroll
+    for (int off = 1; off < NW; off <<= 1) {
+      const uint32_t n = __shfl_up(w, off, 64);
+      if (lane >= off) w += n;
+    }
+    if (lane < NW) wsum[lane] = w;
+  }
+  __syncthreads();
+  if (wave > 0) v += wsum[wave - 1];
+  __syncthreads();
+  return v;
+}
+
+// Given a histogram of nb bins, find the bin holding the krem-th largest
+// element (bins ordered by value).  Thread t owns bins nb-1-2t and nb-2-2t.
+__device__ __forceinline__ void pick_bin(const uint32_t* hist, int nb, uint32_t* wsum,
+                                         uint32_t* sh_digit, uint32_t* sh_krem, uint32_t krem) {
+  const int t = threadIdx.x;
+  const int hi = nb - 1 - 2 * t, lo = nb - 2 - 2 * t;
+  const uint32_t chi = hi >= 0 ? hist[hi] : 0u;
+  const uint32_t clo = lo >= 0 ? hist[lo] : 0u;
+  const uint32_t incl = block_scan_incl(chi + clo, wsum);
+  const uint32_t above = incl - chi - clo;
+  if (hi >= 0 && above < krem && krem <= above + chi) {
+    *sh_digit = static_cast<uint32_t>(hi);
+    *sh_krem = krem - above;
+  } else if (lo >= 0 && above + chi < krem && krem <= incl) {
+    *sh_digit = static_cast<uint32_t>(lo);
+    *sh_krem = krem - above - chi;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(NT) void pool_select_kernel(PrefillArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t sh_digit, sh_krem;
+  __shared__ uint32_t cnt_gt[NW], cnt_eq[NW], eq_before[NW], out_before[NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, bi = blockIdx.y;
+  const size_t g = static_cast<size_t>(bi) * a.Hkv + h;
+  const int m = a.m, p = (a.pool - 1) / 2, K = a.K;
+  const float* raw = a.raw + g * m;
+  float* pooled = a.pooled + g * m;
+  const uint32_t* pbits = reinterpret_cast<const uint32_t*>(pooled);
+
+  for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+  __syncthreads();
+  // pooling + histogram of bits [31:21]
+  for (int i = tid; i < m; i += NT) {
+    const int lo = max(0, i - p), hi = min(m - 1, i + p);
+    float v = raw[lo];
+    for (int u = lo + 1; u <= hi; ++u) v = fmaxf(v, raw[u]);
+    pooled[i] = v;
+    atomicAdd(&hist[__float_as_uint(v) >> 21], 1u);
+  }
+  __syncthreads();
+  if (K == 0) return;
+  pick_bin(hist, 2048, wsum, &sh_digit, &sh_krem, static_cast<uint32_t>(K));
+  uint32_t prefix = sh_digit << 21;
+  uint32_t krem = sh_krem;
+
+  // bits [20:10] among keys whose bits [31:21] match
+  for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < m; i += NT) {
+    const uint32_t v = pbits[i];
+    if ((v >> 21) == (prefix >> 21)) atomicAdd(&hist[(v >> 10) & 0x7ffu], 1u);
+  }
+  __syncthreads();
+  pick_bin(hist, 2048, wsum, &sh_digit, &sh_krem, krem);
+  prefix |= sh_digit << 10;
+  krem = sh_krem;
+
+  // bits [9:0] among keys whose bits [31:10] match
+  for (int i = tid; i < 1024; i += NT) hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < m; i += NT) {
+    const uint32_t v = pbits[i];
+    if ((v >> 10) == (prefix >> 10)) atomicAdd(&hist[v & 0x3ffu], 1u);
+  }
+  __syncthreads();
+  pick_bin(hist, 1024, wsum, &sh_digit, &sh_krem, krem);
+  const uint32_t T = prefix | sh_digit;
+  const uint32_t need_eq = sh_krem;  // keys equal to T that are kept (lowest indices)
+
+  // ordered compaction: wave w scans [w*seg, (w+1)*seg)
+  const int seg = cdiv(cdiv(m, NW), 64) * 64;
+  const int beg = wave * seg, end = min(beg + seg, m);
+  uint32_t ngt = 0, neq = 0;
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    const uint32_t v = i < end ? pbits[i] : 0u;
+    ngt += __popcll(__ballot(i < end && v > T));
+    neq += __popcll(__ballot(i < end && v == T));
+  }
+  if (lane == 0) {
+    cnt_gt[wave] = ngt;
+    cnt_eq[wave] = neq;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t e = 0, o = 0;
+    for (int w = 0; w < NW; ++w) {
+      eq_before[w] = e;
+      out_before[w] = o;
+      const uint32_t take_eq = e >= need_eq ? 0u : min(need_eq - e, cnt_eq[w]);
+      o += cnt_gt[w] + take_eq;
+      e += cnt_eq[w];
+    }
+  }
+  __syncthreads();
+  uint32_t eq_run = eq_before[wave], out_run = out_before[wave];
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int32_t* sel = a.sel + g * K;
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    const uint32_t v = i < end ? pbits[i] : 0u;
+    const bool gt = i < end && v > T;
+    const bool eq = i < end && v == T;
+    const unsigned long long eqm = __ballot(eq);
+    const bool take = gt || (eq && eq_run + __popcll(eqm & below) < need_eq);
+    const unsigned long long tm = __ballot(take);
+    const uint32_t at = out_run + __popcll(tm & below);
+    if (take && at < static_cast<uint32_t>(K)) sel[at] = i;
+    eq_run += __popcll(eqm);
+    out_run += __popcll(tm);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t st) {
+  pool_select_kernel<<<dim3(a.Hkv, a.b), NT, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace ss

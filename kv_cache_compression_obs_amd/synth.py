@@ -113,7 +113,7 @@ def prefill_inputs(w: dict, seed: int, device="cpu", B: int | None = None,
     v = None if w["v_aliases_k"] else _randn(g, (B, Hkv, L, dv), device).to(dt)
     if w["key_lognormal"]:
         k *= torch.exp(0.5 * _randn(g, (B, Hkv, L, 1), device))
-    if w["heavy_keys"]:
+    if w["heavy_keys"] and L > w["C"]:      # planted only where the prompt gets compressed
         ww = dict(w, L=L)
         for b in range(B):
             for h in range(Hkv):
