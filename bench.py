@@ -145,6 +145,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain elementwise copy of this many MiB first (a kernel of "
+                         "known traffic, to calibrate FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this library runs on one GPU "
@@ -160,6 +163,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)       # reads and writes exactly n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.workload(args.workload)
     cfg = ss.make_config(**w)
     B, Hq, L, C = w["B"], w["n_q_heads"], w["L"], w["C"]

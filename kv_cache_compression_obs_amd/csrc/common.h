@@ -10,6 +10,9 @@ namespace ss {
 typedef uint16_t bf16_t;  // raw bfloat16 bits in memory
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// native 16-byte vector (HIP's uint4 class wrapper can keep register arrays
+// from being promoted out of stack memory)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -77,16 +80,16 @@ template <> struct Mma<bf16_t> {  // v_mfma_f32_16x16x32_bf16 (gfx950)
   }
   // 16-byte load of 8 consecutive bf16 values (p must be 16-byte aligned)
   static __device__ __forceinline__ frag load(const bf16_t* p) {
-    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
+    return __builtin_bit_cast(frag, *reinterpret_cast<const u32x4_t*>(p));
   }
   static __device__ __forceinline__ frag zero() {
-    return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0));
+    return __builtin_bit_cast(frag, u32x4_t{0u, 0u, 0u, 0u});
   }
 };
 
 // pack 8 bf16 bit patterns (low index in the low half of each dword)
 __device__ __forceinline__ bf16x8_t pack_bf16x8(const bf16_t* e) {
-  uint4 u;
+  u32x4_t u;
   u.x = static_cast<uint32_t>(e[0]) | (static_cast<uint32_t>(e[1]) << 16);
   u.y = static_cast<uint32_t>(e[2]) | (static_cast<uint32_t>(e[3]) << 16);
   u.z = static_cast<uint32_t>(e[4]) | (static_cast<uint32_t>(e[5]) << 16);

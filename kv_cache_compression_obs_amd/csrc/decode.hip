@@ -188,8 +188,9 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
   const int koff = 4 * (col & 3) + (col >> 2);
 
   frag kf[2][NC];
-  uint4 vr[VLD];
-  auto load_tile = [&](int t0) {
+  u32x4_t vr[VLD];
+  // always inlined: the register arrays it fills must not become stack memory
+  auto load_tile = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int s = min(t0 + 16 * h2 + koff, s1 - 1);
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
     for (int i = 0; i < VLD; ++i) {
       const int id = i * 64 + lane;
       const int s = min(t0 + id / VCH, s1 - 1);
-      vr[i] = *reinterpret_cast<const uint4*>(
+      vr[i] = *reinterpret_cast<const u32x4_t*>(
           reinterpret_cast<const char*>(vb + static_cast<size_t>(s) * VSTRIDE) + (id % VCH) * 16);
     }
   };
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int id = i * 64 + lane;
-      *reinterpret_cast<uint4*>(vt + (id / VCH) * LROW + (id % VCH) * 16) = vr[i];
+      *reinterpret_cast<u32x4_t*>(vt + (id / VCH) * LROW + (id % VCH) * 16) = vr[i];
     }
     frag kcur[2][NC];
 #pragma unroll

@@ -37,21 +37,21 @@ struct KeyTile {
   static_assert((KT * KCH) % SNT == 0, "tile must split evenly over the workgroup");
 
   // rows t0 .. t0+KT-1 of kbase (clamped to kend-1) into registers
-  static __device__ __forceinline__ void load(uint4 (&r)[NLD], const T* kbase, int t0, int kend,
+  static __device__ __forceinline__ void load(u32x4_t (&r)[NLD], const T* kbase, int t0, int kend,
                                               int tid) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int id = i * SNT + tid;
       const int key = min(t0 + id / KCH, kend - 1);
-      r[i] = *reinterpret_cast<const uint4*>(
+      r[i] = *reinterpret_cast<const u32x4_t*>(
           reinterpret_cast<const char*>(kbase + static_cast<size_t>(key) * D) + (id % KCH) * 16);
     }
   }
-  static __device__ __forceinline__ void store(char* buf, const uint4 (&r)[NLD], int tid) {
+  static __device__ __forceinline__ void store(char* buf, const u32x4_t (&r)[NLD], int tid) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int id = i * SNT + tid;
-      *reinterpret_cast<uint4*>(buf + (id / KCH) * LROW + (id % KCH) * 16) = r[i];
+      *reinterpret_cast<u32x4_t*>(buf + (id / KCH) * LROW + (id % KCH) * 16) = r[i];
     }
   }
   // B operand (K^T) fragment: lane (col, qg) takes key 16*kb + col, dims
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(SNT) void score_rowstat_kernel(PrefillArgs a) {
     m[r] = -INFINITY;
     s[r] = 0.f;
   }
-  uint4 ld[KTile::NLD];
+  u32x4_t ld[KTile::NLD];
   KTile::load(ld, kbase, k0, k1, tid);
   KTile::store(lds, ld, tid);
   __syncthreads();
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(SNT) void score_columns_kernel(PrefillArgs a) {
   const T* kbase = static_cast<const T*>(a.k) + gidx * a.L * D;
   float* raw = a.raw + gidx * a.m - a.S;  // indexed by absolute key
 
-  uint4 ld[KTile::NLD];
+  u32x4_t ld[KTile::NLD];
   KTile::load(ld, kbase, k0, k1, tid);
   KTile::store(lds, ld, tid);
   __syncthreads();
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
     const int t = tok[j];
     if (t < 0) continue;
     const size_t s = static_cast<size_t>(sb) * SLOTS + j;
-    *reinterpret_cast<uint4*>(kdst + s * KCH * 16 + ch * 16) =
-        *reinterpret_cast<const uint4*>(ksrc + static_cast<size_t>(t) * KCH * 16 + ch * 16);
+    *reinterpret_cast<u32x4_t*>(kdst + s * KCH * 16 + ch * 16) =
+        *reinterpret_cast<const u32x4_t*>(ksrc + static_cast<size_t>(t) * KCH * 16 + ch * 16);
   }
   if (ALIAS) return;
   const char* vsrc = reinterpret_cast<const char*>(static_cast<const T*>(a.v) + gsrc * a.L * DV);
@@ -316,8 +316,8 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
     const int t = tok[j];
     if (t < 0) continue;
     const size_t s = static_cast<size_t>(sb) * SLOTS + j;
-    *reinterpret_cast<uint4*>(vdst + s * VCH * 16 + ch * 16) =
-        *reinterpret_cast<const uint4*>(vsrc + static_cast<size_t>(t) * VCH * 16 + ch * 16);
+    *reinterpret_cast<u32x4_t*>(vdst + s * VCH * 16 + ch * 16) =
+        *reinterpret_cast<const u32x4_t*>(vsrc + static_cast<size_t>(t) * VCH * 16 + ch * 16);
   }
 }
 
