@@ -80,6 +80,21 @@ def score_flops(w):
     return 2.0 * rows * d * L, 2.0 * rows * d * (L + m)
 
 
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None if there is none for this workload or the kernel sources changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def cpu_baseline(w, inp, dec, budget_s=12.0):
     """The oracle, untuned, on a bounded sample of the same workload."""
     import numpy as np
@@ -182,7 +197,7 @@ def main():
     dec = synth.decode_inputs(w, seed=2, steps=n_dec, device="cuda")
     caches = [ss.Cache(cfg, B) for _ in range(R)]
     ws_p = torch.empty(ss.ss_prefill_workspace_bytes(cfg, B, L), dtype=torch.uint8, device="cuda")
-    ws_d = torch.empty(ss.ss_decode_workspace_bytes(cfg, B), dtype=torch.uint8, device="cuda")
+    ws_d = ss.decode_workspace(cfg, B)
     out = torch.empty(B, Hq, w["d_v"], dtype=dt, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     total_steps = args.warmup + args.steps
@@ -262,13 +277,13 @@ def main():
         "decode_step_us": round(1e6 * dec_call_s, 2),
         "prefill_compress_ms_per_layer": round(sum(pre_ms) / len(pre_ms), 4),
         "roofline": {
-            "kernel": "decode_attend_kernel (split-C flash-decode)",
+            "kernel": "decode_kernel (RoPE + ring scatter + split-C flash-decode + merge)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w["name"]),
             "avg_launch_us": round(1e6 * attn_avg_s, 3),
             "bytes_per_launch": dec_b,
         },

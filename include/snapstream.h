@@ -106,6 +106,15 @@ int32_t ss_cache_slots(const ss_config* cfg);
 size_t ss_prefill_workspace_bytes(const ss_config* cfg, int32_t b, int32_t L);
 size_t ss_decode_workspace_bytes(const ss_config* cfg, int32_t B_max);
 
+/* Prepare a decode workspace before its first ss_decode_step: zero the
+ * per-(row, kv-head) completion counters at its start (one small kernel on
+ * `stream`, no memset, so it may be captured in a graph).  A zero-filled
+ * allocation needs no init.  Every ss_decode_step leaves the counters zero
+ * again, so the workspace stays ready as long as it is used only by
+ * ss_decode_step calls of the same (cfg, B_max), one at a time. */
+ss_status ss_decode_workspace_init(const ss_config* cfg, int32_t B_max, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
 /* Build the fixed cache of b requests at prefill ("Fixed-Size Cache Layout":
  * built once at prefill; SnapKV scoring of the middle by the observation
  * window, sinks and the recent window always kept).
@@ -144,9 +153,13 @@ ss_status ss_prefill_compress(const ss_config* cfg, const void* q_obs, const voi
  *   out    [B_max, n_q_heads, d_v]    attention output, cache dtype
  *   err_flag  optional device int32: set to 1 when an active row has
  *          pos != n_tokens (the step is still applied at pos); never cleared
- *   ws, ws_bytes  device workspace of >= ss_decode_workspace_bytes(cfg, B_max)
+ *   ws, ws_bytes  device workspace of >= ss_decode_workspace_bytes(cfg, B_max),
+ *          zero-filled or prepared by ss_decode_workspace_init before the
+ *          first call (see there); calls sharing a workspace must not overlap
  *
- * Enqueued on `stream`; no host synchronisation, no allocation. */
+ * One kernel: rotary embedding, ring scatter, split-C attention and the merge
+ * of the splits.  Enqueued on `stream`; no host synchronisation, no
+ * allocation. */
 ss_status ss_decode_step(const ss_config* cfg, const void* q, const void* k_new,
                          const void* v_new, const int32_t* pos, const ss_cache* cache,
                          void* out, int32_t* err_flag, void* ws, size_t ws_bytes,

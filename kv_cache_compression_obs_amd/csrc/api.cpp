@@ -3,7 +3,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/snapstream.h"
+#include "snapstream.h"
 #include "launch.h"
 
 namespace {
@@ -38,6 +38,8 @@ ss_status check_config(const ss_config* c) {
   if (c->dtype != SS_F32 && c->dtype != SS_BF16) return SS_ERR_INVALID_ARG;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (!supported_shape(c) || G > 16 || G * c->W > 128) return SS_ERR_UNSUPPORTED;
+  if (c->rope_theta > 0.f && c->rope_end - c->rope_begin > 2 * ss::ROPE_MAX_PAIRS)
+    return SS_ERR_UNSUPPORTED;
   return SS_OK;
 }
 
@@ -84,27 +86,39 @@ PrefillPlan plan_prefill(const ss_config* c, int b, int L) {
 
 // ----------------------------------------------------------------- decode
 struct DecodePlan {
-  int split, n_split;
-  size_t off_q, off_o, off_ml, total;
+  int split, n_split, wsplit;
+  size_t off_cnt, n_cnt, off_o, off_ml, total;
 };
 
 DecodePlan plan_decode(const ss_config* c, int B_max) {
   DecodePlan p{};
   const int C = cache_slots(c);
   const long long groups = static_cast<long long>(B_max) * c->n_kv_heads;
-  // Split the C slots so that the grid holds about 2048 workgroups (8 per CU
-  // on 256 CUs) when every slot is valid; at least one 32-slot tile each.
-  int tiles = (C + ss::DECODE_TILE - 1) / ss::DECODE_TILE;
-  long long want = (2048 + groups - 1) / groups;
+  // Each workgroup of DECODE_WAVES waves takes a split of the C slots, each
+  // wave 1 to DECODE_MAX_TILES tiles of 32 slots, so that the grid holds
+  // about DECODE_TARGET_WAVES waves when every slot is valid (short splits
+  // balance rows of very different valid lengths).
+  const long long tiles = (C + ss::DECODE_TILE - 1) / ss::DECODE_TILE;
+  long long want = (ss::DECODE_TARGET_WAVES + groups - 1) / groups;  // waves per group
   if (want < 1) want = 1;
-  int tiles_per_split = static_cast<int>((tiles + want - 1) / want);
-  if (tiles_per_split < 1) tiles_per_split = 1;
-  p.split = tiles_per_split * ss::DECODE_TILE;
+  long long tpw = (tiles + want - 1) / want;
+  if (tpw > ss::DECODE_MAX_TILES) tpw = ss::DECODE_MAX_TILES;
+  if (tpw < 1) tpw = 1;
+  // the merge keeps G weights per split in the workgroup's V tiles (LDS)
+  const int G = c->n_q_heads / c->n_kv_heads;
+  const int es = c->dtype == SS_BF16 ? 2 : 4;
+  const long long max_splits = ss::decode_merge_capacity(c->d_v * es) / G;
+  const long long min_tpw =
+      (tiles + max_splits * ss::DECODE_WAVES - 1) / (max_splits * ss::DECODE_WAVES);
+  if (tpw < min_tpw) tpw = min_tpw;
+  p.wsplit = static_cast<int>(tpw) * ss::DECODE_TILE;
+  p.split = ss::DECODE_WAVES * p.wsplit;
   p.n_split = (C + p.split - 1) / p.split;
   const size_t rows_q = static_cast<size_t>(B_max) * c->n_q_heads;
   size_t off = 0;
-  p.off_q = off;
-  off += align_up(rows_q * c->d_qk * sizeof(float));
+  p.off_cnt = off;
+  p.n_cnt = static_cast<size_t>(groups);
+  off += align_up(p.n_cnt * sizeof(int32_t));
   p.off_o = off;
   off += align_up(rows_q * p.n_split * c->d_v * sizeof(float));
   p.off_ml = off;
@@ -132,6 +146,19 @@ size_t ss_prefill_workspace_bytes(const ss_config* cfg, int32_t b, int32_t L) {
 size_t ss_decode_workspace_bytes(const ss_config* cfg, int32_t B_max) {
   if (check_config(cfg) != SS_OK || B_max < 1) return 0;
   return plan_decode(cfg, B_max).total;
+}
+
+ss_status ss_decode_workspace_init(const ss_config* cfg, int32_t B_max, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  const ss_status cs = check_config(cfg);
+  if (cs != SS_OK) return cs;
+  if (B_max < 1) return SS_ERR_INVALID_ARG;
+  const DecodePlan p = plan_decode(cfg, B_max);
+  if (ws == nullptr || ws_bytes < p.total) return SS_ERR_WORKSPACE;
+  int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.off_cnt);
+  if (ss::launch_zero_counters(cnt, static_cast<int>(p.n_cnt), stream) != hipSuccess)
+    return SS_ERR_HIP;
+  return SS_OK;
 }
 
 }  // extern "C"
@@ -232,7 +259,7 @@ ss_status decode_impl(const ss_config* cfg, const void* q, const void* k_new, co
   a.n_tokens = cache->n_tokens;
   a.out = out;
   a.err = err_flag;
-  a.q_rot = reinterpret_cast<float*>(w + p.off_q);
+  a.counter = reinterpret_cast<int32_t*>(w + p.off_cnt);
   a.part_o = reinterpret_cast<float*>(w + p.off_o);
   a.part_ml = reinterpret_cast<float*>(w + p.off_ml);
   a.B = cache->B_max;
@@ -245,10 +272,13 @@ ss_status decode_impl(const ss_config* cfg, const void* q, const void* k_new, co
   a.R = cfg->L_recent;
   a.split = p.split;
   a.n_split = p.n_split;
+  a.wsplit = p.wsplit;
   a.scale_log2 = scale_log2(cfg);
-  a.rope_theta = cfg->rope_theta;
   a.rope_begin = cfg->rope_begin;
-  a.rope_end = cfg->rope_end;
+  a.rope_half = cfg->rope_theta > 0.f ? (cfg->rope_end - cfg->rope_begin) / 2 : 0;
+  for (int i = 0; i < a.rope_half; ++i)  // libm pow, as in the oracle
+    a.inv_freq[i] = pow(static_cast<double>(cfg->rope_theta),
+                        -2.0 * i / (cfg->rope_end - cfg->rope_begin));
   if (ss::launch_decode(cfg->dtype, cfg->d_qk, cfg->d_v, cfg->v_aliases_k, a, stream, ev0, ev1) !=
       hipSuccess)
     return SS_ERR_HIP;

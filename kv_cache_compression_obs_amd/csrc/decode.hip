@@ -1,6 +1,6 @@
-// Decode step over the fixed-size cache: rotary embedding + ring-buffer
-// scatter of the new token, split-C flash-decode attention with GQA head
-// grouping on MFMA, and a fixed-order combine of the split partials.
+// Decode step over the fixed-size cache, as one kernel: rotary embedding of
+// the new token, its ring-buffer scatter, split-C flash-decode attention with
+// GQA head grouping on MFMA, and the merge of the split partials.
 //
 // Follows "SnapStream: Taming KV-Cache Eviction for Dataflow Accelerators",
 // sections "Ring Buffer vs. Naive Slicing" (decode rotates only the recent
@@ -14,78 +14,33 @@ namespace ss {
 
 namespace {
 
-// Rotate-half rotary embedding of element d of a row, computed in fp64 from
-// the stored values and rounded once to O (the cache dtype for keys, fp32 for
-// queries).  cs/sn hold cos/sin of the pair angles (pair i couples dims
-// begin+i and begin+i+half).
+// Rotate-half rotary embedding of element d of a row (value x, and xp = the
+// element it pairs with), computed in fp64 from the stored values and rounded
+// once to O (the cache dtype for keys, fp32 for queries).  cs/sn hold cos/sin
+// of the pair angles (pair i couples dims begin+i and begin+i+half).
 template <typename T, typename O>
-__device__ __forceinline__ O rotate_elem(const T* row, int d, bool rope, int begin, int half,
+__device__ __forceinline__ O rotate_pair(T x, T xp, int d, bool rope, int begin, int half,
                                          const double* cs, const double* sn) {
-  if (!rope || d < begin || d >= begin + 2 * half) return from_f32<O>(to_f32<T>(row[d]));
+  if (!rope || d < begin || d >= begin + 2 * half) return from_f32<O>(to_f32<T>(x));
   const int i = d - begin;
-  if (i < half) {
-    const double x1 = to_f32<T>(row[d]), x2 = to_f32<T>(row[d + half]);
-    return from_f64<O>(x1 * cs[i] - x2 * sn[i]);
-  }
-  const double x2 = to_f32<T>(row[d]), x1 = to_f32<T>(row[d - half]);
-  return from_f64<O>(x2 * cs[i - half] + x1 * sn[i - half]);
+  const double v = to_f32<T>(x), w = to_f32<T>(xp);
+  if (i < half) return from_f64<O>(v * cs[i] - w * sn[i]);
+  return from_f64<O>(v * cs[i - half] + w * sn[i - half]);
 }
 
-// One workgroup per cache row: rotate q (into the workspace) and k_new at the
-// absolute position, write k_new/v_new into the ring slot, update slot_pos
-// and n_tokens.  Inactive rows (pos < 0) are left untouched.
-template <typename T, int D, int DV, bool ALIAS>
-__global__ __launch_bounds__(256) void decode_scatter_kernel(DecodeArgs a) {
-  const int b = blockIdx.x;
-  const int p = a.pos[b];
-  if (p < 0) return;
-  __shared__ double cs[D / 2], sn[D / 2];
-  const bool rope = a.rope_theta > 0.0;
-  const int d_rot = a.rope_end - a.rope_begin;
-  const int half = rope ? d_rot / 2 : 0;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const double ang = static_cast<double>(p) * pow(a.rope_theta, -2.0 * i / d_rot);
-    double s, c;
-    sincos(ang, &s, &c);
-    cs[i] = c;
-    sn[i] = s;
-  }
-  if (threadIdx.x == 0) {
-    if (a.err != nullptr && a.n_tokens[b] != p) atomicOr(a.err, 1);
-    a.n_tokens[b] = p + 1;
-  }
-  __syncthreads();
-  const int SK = a.S + a.K;
-  const int slot = p < SK ? p : SK + (p - SK) % a.R;
-
-  const T* q = static_cast<const T*>(a.q) + static_cast<size_t>(b) * a.Hq * D;
-  float* qr = a.q_rot + static_cast<size_t>(b) * a.Hq * D;
-  for (int idx = threadIdx.x; idx < a.Hq * D; idx += blockDim.x) {
-    const int d = idx % D;
-    qr[idx] = rotate_elem<T, float>(q + (idx - d), d, rope, a.rope_begin, half, cs, sn);
-  }
-  const T* kn = static_cast<const T*>(a.k_new) + static_cast<size_t>(b) * a.Hkv * D;
-  T* kc = static_cast<T*>(a.kc);
-  for (int idx = threadIdx.x; idx < a.Hkv * D; idx += blockDim.x) {
-    const int h = idx / D, d = idx % D;
-    const size_t dst = ((static_cast<size_t>(b) * a.Hkv + h) * a.C + slot) * D + d;
-    kc[dst] = rotate_elem<T, T>(kn + (idx - d), d, rope, a.rope_begin, half, cs, sn);
-  }
-  if (!ALIAS) {
-    const T* vn = static_cast<const T*>(a.v_new) + static_cast<size_t>(b) * a.Hkv * DV;
-    T* vc = static_cast<T*>(a.vc);
-    for (int idx = threadIdx.x; idx < a.Hkv * DV; idx += blockDim.x) {
-      const int h = idx / DV, d = idx % DV;
-      vc[((static_cast<size_t>(b) * a.Hkv + h) * a.C + slot) * DV + d] = vn[idx];
-    }
-  }
-  for (int h = threadIdx.x; h < a.Hkv; h += blockDim.x)
-    a.slot_pos[(static_cast<size_t>(b) * a.Hkv + h) * a.C + slot] = p;
+// Device-scope stores: written through to the level shared by all XCDs (the
+// sc1 policy the compiler uses for agent-scope atomic stores), so publishing
+// them needs no whole-L2 write-back.  Completion is awaited with s_waitcnt.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev4(float* p, f32x4_t v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
 // Operands of the P.V contraction.  The contraction index of lane group qg,
 // element i is the tile-local slot 4*i + qg (i < 8), which is exactly where
-// the Q.K^T accumulator left that slot's probability (see decode_attend).
+// the Q.K^T accumulator left that slot's probability (see decode_kernel).
 template <typename T> struct PvOps;
 
 template <> struct PvOps<bf16_t> {
@@ -133,16 +88,41 @@ template <> struct Split<bf16_t> {
   }
 };
 
-// Split-C flash-decode.  One wave per (split, kv-head, row); the G q-heads of
-// the kv-head share every K/V byte read.  Per 32-slot tile:
-//   S^T[slot, head] = K[slot, :] . Q[head, :]^T    (MFMA, K rows straight from HBM)
+constexpr int DW = DECODE_WAVES;  // waves per decode workgroup
+
+// Orders LDS accesses of one wave (a wave executes its LDS instructions in
+// order; this keeps the compiler from moving them across the point).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One workgroup of DW waves per (split of the slots, kv-head, row); wave w
+// streams the w-th quarter of the split.
+//
+// Prologue (whole workgroup): rotate the G queries of the kv-head at pos (fp64
+// angles) into LDS; the workgroup whose split holds the ring slot of pos also
+// rotates k_new, writes it and v_new into that slot of the cache (evicting
+// pos - L_recent), sets slot_pos, and (kv-head 0) checks and advances
+// n_tokens.  The wave that meets the new row in its tiles takes it from LDS,
+// so nothing reads back what this launch wrote to HBM.
+//
+// Main loop, per wave and 32-slot tile (the G q-heads share every K/V byte):
+//   S^T[slot, head] = K[slot, :] . Q[head, :]^T     MFMA, K rows straight from HBM
 //   online softmax over slots per head (log2 domain)
-//   O^T[dv, head] += V^T[dv, slot] . P^T[slot, head]  (MFMA, V staged in LDS)
+//   O^T[dv, head] += V^T[dv, slot] . P^T[slot, head]  MFMA, V staged in LDS
 // K rows are loaded in the order slot = t0 + 16*h2 + 4*(m%4) + m/4 for A-row m,
 // so accumulator register r of lane group qg holds slot t0 + 16*h2 + 4*r + qg:
-// the probabilities are already in the P^T operand layout, no shuffle needed.
+// the probabilities are already in the P^T operand layout.
+//
+// Epilogue: the DW wave partials are merged in LDS into the workgroup's
+// (max, sum, unnormalised output) partial, written through to the level
+// shared by all XCDs; the last workgroup of the (row, kv-head) to take a
+// ticket (device-scope counter) merges every split in split order and resets
+// the counter.
 template <typename T, int D, int DV, bool ALIAS>
-__global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   using MM = Mma<T>;
   using frag = typename MM::frag;
   constexpr int KPL = MM::KPL, KSTEP = MM::KSTEP;
@@ -151,49 +131,57 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
   constexpr int TS = DECODE_TILE;
   constexpr int VROW = DV * static_cast<int>(sizeof(T));
   constexpr int VSTRIDE = ALIAS ? D : DV;
-  constexpr int LROW = VROW + 32;
+  constexpr int LROW = decode_vrow_stride(VROW);
   constexpr int VCH = VROW / 16;
   constexpr int VLD = TS * VCH / 64;
+  constexpr int NP = Split<T>::N;
+  constexpr int WBYTES = TS * LROW;  // one wave's V tile
   static_assert(D % KSTEP == 0 && DV % 64 == 0 && (TS * VCH) % 64 == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) char vt[TS * LROW];
+  static_assert(DW * WBYTES >= 16 * D * 4, "query staging must fit in the V tiles");
+  static_assert(WBYTES >= 16 * DV * 4, "a wave's partial must fit in its V tile");
+  __shared__ __attribute__((aligned(16))) char vt_all[DW * WBYTES];
+  __shared__ double csn[D];
+  __shared__ __attribute__((aligned(16))) T knew[D];
+  __shared__ __attribute__((aligned(16))) T vnew[DV];
+  __shared__ float wm[DW][16], wl[DW][16];
+  __shared__ int sh_ticket;
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.G;
   const int p = a.pos[b];
-  if (p < 0) return;
+  const size_t gh = static_cast<size_t>(b) * a.Hkv + h;
+  const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(h) * G;
+  if (p < 0) {  // inactive row: output 0, no state change
+    if (split == 0) {
+      T* o = static_cast<T*>(a.out) + head0 * DV;
+      for (int i = tid; i < G * DV; i += 64 * DW) o[i] = from_f32<T>(0.f);
+    }
+    return;
+  }
   const int n_valid = min(p + 1, a.C);
+  const int ns = cdiv(n_valid, a.split);
+  if (split >= ns) return;
   const int s0 = split * a.split;
-  if (s0 >= n_valid) return;
   const int s1 = min(s0 + a.split, n_valid);
+  const int w0 = min(s0 + wave * a.wsplit, s1);  // this wave's slots [w0, w1)
+  const int w1 = min(w0 + a.wsplit, s1);
+  const int SK = a.S + a.K;
+  const int slot = p < SK ? p : SK + (p - SK) % a.R;
+  const bool own = slot >= s0 && slot < s1;
+  const bool wown = slot >= w0 && slot < w1;
   const int col = lane & 15, qg = lane >> 4;
 
-  constexpr int NP = Split<T>::N;
-  const float* qrow =
-      a.q_rot + (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(h) * a.G + col) * D;
-  frag qf[NP][NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    float qv[KPL];
-#pragma unroll
-    for (int e = 0; e < KPL; ++e) qv[e] = (col < a.G) ? qrow[c * KSTEP + qg * KPL + e] : 0.f;
-    frag parts[NP];
-    Split<T>::make(qv, parts);
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) qf[pp][c] = parts[pp];
-  }
-
-  const size_t gh = static_cast<size_t>(b) * a.Hkv + h;
   const T* kb = static_cast<const T*>(a.kc) + gh * a.C * D;
   const T* vb = ALIAS ? kb : static_cast<const T*>(a.vc) + gh * a.C * DV;
   const int koff = 4 * (col & 3) + (col >> 2);
-
   frag kf[2][NC];
   u32x4_t vr[VLD];
   // always inlined: the register arrays it fills must not become stack memory
   auto load_tile = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int s = min(t0 + 16 * h2 + koff, s1 - 1);
+      const int s = min(t0 + 16 * h2 + koff, w1 - 1);
       const T* kr = kb + static_cast<size_t>(s) * D + qg * KPL;
 #pragma unroll
       for (int c = 0; c < NC; ++c) kf[h2][c] = MM::load(kr + c * KSTEP);
@@ -201,20 +189,128 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int id = i * 64 + lane;
-      const int s = min(t0 + id / VCH, s1 - 1);
+      const int s = min(t0 + id / VCH, w1 - 1);
       vr[i] = *reinterpret_cast<const u32x4_t*>(
           reinterpret_cast<const char*>(vb + static_cast<size_t>(s) * VSTRIDE) + (id % VCH) * 16);
     }
   };
+  // ---------------------------------------------------------------- RoPE
+  // The new token's q / k_new / v_new elements (and their rotation partners)
+  // are loaded first, then the first tile is requested: vector loads complete
+  // in issue order, so the rotary work does not wait for the tile, while the
+  // tile's latency covers the rotary work.  If the tile holds the new token's
+  // slot, the stale row it reads is replaced from LDS in the main loop.
+  const int half = a.rope_half;
+  const bool rope = half > 0;
+  const int rb = a.rope_begin;
+  auto partner = [&](int d) __attribute__((always_inline)) {
+    if (!rope || d < rb || d >= rb + 2 * half) return d;
+    return d - rb < half ? d + half : d - half;
+  };
+  constexpr int NT = 64 * DW;
+  constexpr int QPT = cdiv(16 * D, NT), KPT = cdiv(D, NT), VPT = cdiv(DV, NT);
+  T qx[QPT], qp[QPT], kx[KPT], kp[KPT], vx[VPT];
+  {
+    const T* q = static_cast<const T*>(a.q) + head0 * D;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int idx = tid + j * NT;
+      if (idx < G * D) {
+        const int d = idx % D;
+        qx[j] = q[idx];
+        qp[j] = q[idx - d + partner(d)];
+      }
+    }
+    if (own) {
+      const T* kn = static_cast<const T*>(a.k_new) + gh * D;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int d = tid + j * NT;
+        if (d < D) {
+          kx[j] = kn[d];
+          kp[j] = kn[partner(d)];
+        }
+      }
+      if (!ALIAS) {
+        const T* vn = static_cast<const T*>(a.v_new) + gh * DV;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+          if (tid + j * NT < DV) vx[j] = vn[tid + j * NT];
+      }
+    }
+  }
+  if (w0 < w1) load_tile(w0);
+  for (int i = tid; i < half; i += NT) {
+    const double ang = static_cast<double>(p) * a.inv_freq[i];
+    double sv, cv;
+    sincos(ang, &sv, &cv);
+    csn[i] = cv;
+    csn[half + i] = sv;
+  }
+  __syncthreads();
+  float* qs = reinterpret_cast<float*>(vt_all);  // [G, D] rotated queries, fp32
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int idx = tid + j * NT;
+    if (idx < G * D)
+      qs[idx] = rotate_pair<T, float>(qx[j], qp[j], idx % D, rope, rb, half, csn, csn + half);
+  }
+  if (own) {
+    T* kdst = static_cast<T*>(a.kc) + (gh * a.C + slot) * D;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int d = tid + j * NT;
+      if (d < D) {
+        const T kv = rotate_pair<T, T>(kx[j], kp[j], d, rope, rb, half, csn, csn + half);
+        knew[d] = kv;
+        kdst[d] = kv;
+      }
+    }
+    if (!ALIAS) {
+      T* vdst = static_cast<T*>(a.vc) + (gh * a.C + slot) * DV;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int d = tid + j * NT;
+        if (d < DV) {
+          vnew[d] = vx[j];
+          vdst[d] = vx[j];
+        }
+      }
+    }
+    if (tid == 0) {
+      a.slot_pos[gh * a.C + slot] = p;
+      if (h == 0) {
+        if (a.err != nullptr && a.n_tokens[b] != p) atomicOr(a.err, 1);
+        a.n_tokens[b] = p + 1;
+      }
+    }
+  }
+  __syncthreads();
+  if (ALIAS && own)  // the value is the first DV dims of the new latent row
+    for (int d = tid; d < DV; d += 64 * DW) vnew[d] = knew[d];
 
+  frag qf[NP][NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float qv[KPL];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) qv[e] = col < G ? qs[col * D + c * KSTEP + qg * KPL + e] : 0.f;
+    frag parts[NP];
+    Split<T>::make(qv, parts);
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) qf[pp][c] = parts[pp];
+  }
+  __syncthreads();  // queries read (their LDS is the V tiles) and vnew ready
+
+  // ------------------------------------------------- main loop (per wave)
+  char* vt = vt_all + wave * WBYTES;
   f32x4_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  load_tile(s0);
-  for (int t0 = s0; t0 < s1; t0 += TS) {
-    __syncthreads();  // the previous tile's LDS reads are done
+  for (int t0 = w0; t0 < w1; t0 += TS) {
+    wave_sync();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int id = i * 64 + lane;
@@ -225,7 +321,20 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int c = 0; c < NC; ++c) kcur[h2][c] = kf[h2][c];
-    if (t0 + TS < s1) load_tile(t0 + TS);  // next tile in flight during this one
+    if (wown && slot >= t0 && slot < t0 + TS) {
+      // the new token: every tile row whose (clamped) slot is `slot` takes it
+      // from LDS, never from the cache memory this launch just wrote
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        if (min(t0 + 16 * h2 + koff, w1 - 1) == slot)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) kcur[h2][c] = MM::load(knew + c * KSTEP + qg * KPL);
+      for (int r = 0; r < TS; ++r)
+        if (min(t0 + r, w1 - 1) == slot)
+          for (int i = lane; i < VROW / 4; i += 64)
+            reinterpret_cast<uint32_t*>(vt + r * LROW)[i] = reinterpret_cast<const uint32_t*>(vnew)[i];
+    }
+    if (t0 + TS < w1) load_tile(t0 + TS);  // next tile in flight during this one
 
     f32x4_t sacc[2];
 #pragma unroll
@@ -241,7 +350,7 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = t0 + 4 * i + qg;  // i = 4*h2 + r  ->  slot t0 + 16*h2 + 4*r + qg
-      x[i] = s < s1 ? sacc[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+      x[i] = s < w1 ? sacc[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, x[i]);
     }
     tmax = xor_max(tmax, 16);
@@ -261,7 +370,7 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
     frag pfr[PST][NP];
 #pragma unroll
     for (int st = 0; st < PST; ++st) Split<T>::make(pf + st * KPL, pfr[st]);
-    __syncthreads();  // V tile visible in LDS
+    wave_sync();  // V tile written before the transposed reads
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       oacc[db] *= alpha;
@@ -275,61 +384,109 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(DecodeArgs a) {
   }
   l_run = xor_sum(l_run, 16);
   l_run = xor_sum(l_run, 32);
-  if (col < a.G) {
-    const size_t pidx =
-        (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(h) * a.G + col) * a.n_split + split;
-    float* po = a.part_o + pidx * DV;
+
+  // ------------------------------------------------------------ epilogue
+  // the wave's partial into its own V tile (its loop is over), [G][DV] fp32
+  wave_sync();
+  float* wo = reinterpret_cast<float*>(vt);
+  if (col < G) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<float4*>(po + 16 * db + 4 * qg) =
-          make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+      *reinterpret_cast<f32x4_t*>(wo + col * DV + 16 * db + 4 * qg) = oacc[db];
     if (qg == 0) {
-      a.part_ml[2 * pidx] = m_run;
-      a.part_ml[2 * pidx + 1] = l_run;
+      wm[wave][col] = m_run;  // -inf for a wave without slots
+      wl[wave][col] = l_run;
     }
   }
+  __syncthreads();
+  // workgroup partial = merge of the DW wave partials; written with
+  // device-scope stores (see st_dev)
+  for (int idx = tid; idx < G * (DV / 4); idx += 64 * DW) {
+    const int g = idx / (DV / 4), d4 = idx % (DV / 4);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < DW; ++w) M = fmaxf(M, wm[w][g]);
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < DW; ++w)
+      o += exp2f(wm[w][g] - M) *
+           *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(vt_all + w * WBYTES) +
+                                            g * DV + 4 * d4);
+    st_dev4(a.part_o + ((head0 + g) * a.n_split + split) * DV + 4 * d4, o);
+  }
+  if (tid < G) {
+    float M = -INFINITY, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < DW; ++w) M = fmaxf(M, wm[w][tid]);
+#pragma unroll
+    for (int w = 0; w < DW; ++w) L += exp2f(wm[w][tid] - M) * wl[w][tid];
+    const size_t pidx = (head0 + tid) * a.n_split + split;
+    st_dev(a.part_ml + 2 * pidx, M);
+    st_dev(a.part_ml + 2 * pidx + 1, L);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();                // ... and every other thread's
+  if (tid == 0)
+    sh_ticket = __hip_atomic_fetch_add(a.counter + gh, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sh_ticket != ns - 1) return;
+  // Acquire once (drops this XCD's stale L2 lines), then ordinary loads.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // out[head, dv] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, in split
+  // order.  Each thread loads every split's (m, l, o) of its 4 outputs at
+  // once (batches of MB splits), so the merge costs one memory round trip
+  // per batch rather than one per dependent step.
+  constexpr int MB = 16;
+  for (int idx = tid; idx < G * (DV / 4); idx += 64 * DW) {
+    const int g = idx / (DV / 4), d4 = idx % (DV / 4);
+    const size_t base = (head0 + g) * a.n_split;
+    float M = -INFINITY, L = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < ns; sb += MB) {
+      float mv[MB], lv[MB];
+      f32x4_t ov[MB];
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const bool in = sb + j < ns;
+        const size_t s = base + sb + (in ? j : 0);
+        mv[j] = in ? a.part_ml[2 * s] : -INFINITY;
+        lv[j] = in ? a.part_ml[2 * s + 1] : 0.f;
+        ov[j] = in ? *reinterpret_cast<const f32x4_t*>(a.part_o + s * DV + 4 * d4)
+                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) Mn = fmaxf(Mn, mv[j]);
+      const float r = exp2f(M - Mn);
+      L *= r;
+      acc *= r;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const float w = exp2f(mv[j] - Mn);
+        L += w * lv[j];
+        acc += w * ov[j];
+      }
+      M = Mn;
+    }
+    const float inv = 1.f / L;
+    T* o = static_cast<T*>(a.out) + (head0 + g) * DV + 4 * d4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(acc[e] * inv);
+  }
+  if (tid == 0) a.counter[gh] = 0;  // ready for the next call
 }
 
-// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the non-empty
-// splits of the row, in split order (deterministic).  Inactive rows get 0.
-template <typename T, int DV>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int PER = DV / 64;
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  T* out = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.Hq + hq) * DV + lane * PER;
-  const int p = a.pos[b];
-  if (p < 0) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) out[e] = from_f32<T>(0.f);
-    return;
-  }
-  const int ns = cdiv(min(p + 1, a.C), a.split);
-  const size_t base = (static_cast<size_t>(b) * a.Hq + hq) * a.n_split;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[2 * (base + s)]);
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float wsum = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = exp2f(a.part_ml[2 * (base + s)] - M);
-    wsum += w * a.part_ml[2 * (base + s) + 1];
-    const float* po = a.part_o + (base + s) * DV + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * po[e];
-  }
-  const float inv = 1.f / wsum;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) out[e] = from_f32<T>(acc[e] * inv);
+__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* c, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) c[i] = 0;
 }
 
 template <typename T, int D, int DV, bool ALIAS>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  decode_scatter_kernel<T, D, DV, ALIAS><<<a.B, 256, 0, st>>>(a);
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
-  decode_attend_kernel<T, D, DV, ALIAS><<<dim3(a.n_split, a.Hkv, a.B), 64, 0, st>>>(a);
+  decode_kernel<T, D, DV, ALIAS><<<dim3(a.n_split, a.Hkv, a.B), 64 * DW, 0, st>>>(a);
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
-  decode_combine_kernel<T, DV><<<dim3(a.Hq, a.B), 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -345,6 +502,11 @@ hipError_t launch_decode(int dtype, int D, int DV, int alias, const DecodeArgs& 
   if (dtype == 1 && D == 128 && DV == 128)
     return run_decode<bf16_t, 128, 128, false>(a, st, ev0, ev1);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t st) {
+  zero_counters_kernel<<<cdiv(n, 256), 256, 0, st>>>(counters, n);
+  return hipGetLastError();
 }
 
 }  // namespace ss

@@ -6,6 +6,8 @@
 
 namespace ss {
 
+constexpr int ROPE_MAX_PAIRS = 64;  // rotary range of at most 128 dims
+
 struct DecodeArgs {
   const void* q;         // [B, Hq, D] pre-RoPE
   const void* k_new;     // [B, Hkv, D] pre-RoPE
@@ -17,14 +19,16 @@ struct DecodeArgs {
   int32_t* n_tokens;     // [B]
   void* out;             // [B, Hq, DV]
   int32_t* err;          // optional
-  float* q_rot;          // ws: rotated queries [B, Hq, D], fp32
   float* part_o;         // ws: [B, Hq, n_split, DV] unnormalised partial outputs
   float* part_ml;        // ws: [B, Hq, n_split, 2] (running max in log2 units, sum)
+  int32_t* counter;      // ws: [B, Hkv] finished-split counters, zero between calls
   int B, Hq, Hkv, G, C, S, K, R;
-  int split, n_split;    // slots per split (multiple of 32), number of splits
+  int split, n_split;    // slots per workgroup split, number of splits
+  int wsplit;            // slots per wave (multiple of 32); split = DECODE_WAVES * wsplit
   float scale_log2;      // softmax scale * log2(e)
-  double rope_theta;     // 0: no rotation
-  int rope_begin, rope_end;
+  int rope_begin;        // rotated dims [rope_begin, rope_begin + 2*rope_half)
+  int rope_half;         // rotation pairs; 0: no rotation
+  double inv_freq[ROPE_MAX_PAIRS];  // theta^(-2i/d_rot), computed on the host
 };
 
 struct PrefillArgs {
@@ -54,12 +58,31 @@ hipError_t launch_decode(int dtype, int D, int DV, int alias, const DecodeArgs& 
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStream_t st,
                                  hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t st);
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_gather(int dtype, int D, int DV, int alias, bool compressed,
                                  const PrefillArgs& a, hipStream_t st);
 
 // Tiling constants the host uses to size workspaces.
 constexpr int DECODE_TILE = 32;   // slots per decode tile
+constexpr int DECODE_WAVES = 4;   // waves per decode workgroup
+// Decode grid: aim for this many waves when every slot is valid, with at most
+// this many tiles per wave (compile-time tunables).
+#ifndef SS_DECODE_TARGET_WAVES
+#define SS_DECODE_TARGET_WAVES 2048
+#endif
+#ifndef SS_DECODE_MAX_TILES
+#define SS_DECODE_MAX_TILES 32
+#endif
+constexpr int DECODE_TARGET_WAVES = SS_DECODE_TARGET_WAVES;
+constexpr int DECODE_MAX_TILES = SS_DECODE_MAX_TILES;
+// LDS row stride of the decode V tile (bytes) for value rows of `row_bytes`;
+// the workgroup's V tiles are reused for the merge weights, so a plan must
+// keep G * n_split <= decode_merge_capacity().
+constexpr int decode_vrow_stride(int row_bytes) { return row_bytes + 32; }
+constexpr int decode_merge_capacity(int row_bytes) {
+  return DECODE_WAVES * DECODE_TILE * decode_vrow_stride(row_bytes) / 4;
+}
 constexpr int SCORE_KT_MAX = 64;  // keys per score tile (chunks are multiples of it)
 
 }  // namespace ss

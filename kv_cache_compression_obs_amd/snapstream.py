@@ -19,8 +19,8 @@ DTYPES = {"f32": SS_F32, "bf16": SS_BF16}
 TORCH_DTYPE = {SS_F32: torch.float32, SS_BF16: torch.bfloat16}
 
 EXPORTS = ("ss_cache_slots", "ss_prefill_workspace_bytes", "ss_decode_workspace_bytes",
-           "ss_prefill_compress", "ss_decode_step", "ss_prefill_compress_timed",
-           "ss_decode_step_timed", "ss_status_string")
+           "ss_decode_workspace_init", "ss_prefill_compress", "ss_decode_step",
+           "ss_prefill_compress_timed", "ss_decode_step_timed", "ss_status_string")
 
 
 class ss_config(ctypes.Structure):
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.ss_prefill_compress_timed.restype = I32
         L.ss_decode_step_timed.argtypes = L.ss_decode_step.argtypes + [VP, VP]
         L.ss_decode_step_timed.restype = I32
+        L.ss_decode_workspace_init.argtypes = [P(ss_config), I32, VP, SZ, VP]
+        L.ss_decode_workspace_init.restype = I32
         L.ss_status_string.argtypes = [I32]
         L.ss_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -124,6 +126,19 @@ def ss_prefill_workspace_bytes(cfg: ss_config, b: int, L: int) -> int:
 
 def ss_decode_workspace_bytes(cfg: ss_config, B_max: int) -> int:
     return lib().ss_decode_workspace_bytes(ctypes.byref(cfg), int(B_max))
+
+
+def ss_decode_workspace_init(cfg: ss_config, B_max: int, ws, stream=None) -> None:
+    _check(ws, "ws", torch.uint8)
+    st = lib().ss_decode_workspace_init(ctypes.byref(cfg), int(B_max), _ptr(ws), ws.numel(),
+                                        _stream(stream))
+    if st != SS_OK:
+        raise SnapStreamError(st, "ss_decode_workspace_init")
+
+
+def decode_workspace(cfg: ss_config, B_max: int, device="cuda"):
+    """A decode workspace ready for its first ss_decode_step (zero-filled)."""
+    return torch.zeros(ss_decode_workspace_bytes(cfg, B_max), dtype=torch.uint8, device=device)
 
 
 class Cache:
@@ -194,8 +209,7 @@ def ss_decode_step(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, out, err_
     _check(pos, "pos", torch.int32)
     _check(err_flag, "err_flag", torch.int32)
     if ws is None:
-        ws = torch.empty(ss_decode_workspace_bytes(cfg, cache.B_max), dtype=torch.uint8,
-                         device=q.device)
+        ws = decode_workspace(cfg, cache.B_max, q.device)
     cs = cache.struct()
     args = (ctypes.byref(cfg), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), ctypes.byref(cs),
             _ptr(out), _ptr(err_flag), _ptr(ws), ws.numel(), _stream(stream))

@@ -34,7 +34,10 @@ def _decode_case(w, L, steps, seed, B=None, positions=None, check_every=1):
     dt = synth.TORCH_DTYPE[w["dtype"]]
     out = torch.empty(B, w["n_q_heads"], w["d_v"], dtype=dt, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ws = torch.empty(ss.ss_decode_workspace_bytes(cfg_l, B), dtype=torch.uint8, device="cuda")
+    # an uninitialised workspace made ready by the library's own init call
+    ws = torch.full((ss.ss_decode_workspace_bytes(cfg_l, B),), 0xA5, dtype=torch.uint8,
+                    device="cuda")
+    ss.ss_decode_workspace_init(cfg_l, B, ws)
     tol = OUT_TOL[w["dtype"]]
     worst = 0.0
     for t in range(steps):
@@ -142,3 +145,31 @@ def test_decode_llama8b_c4k_full_shape():
     _say("decode llama8b_c4k full B=16 L=16384 steps=3")
     worst = _decode_case(w, L=w["L"], steps=3, seed=8)
     _say(f"  worst max-abs {worst:.3g}")
+
+
+def test_decode_is_deterministic_and_workspace_reusable():
+    # same inputs on two copies of the cache give bitwise-identical outputs
+    # (fixed split order), and a workspace reused for many calls stays valid
+    w = synth.workload("llama8b_c4k", B=4, L_sink=16, K=240, L_recent=256)
+    cfg = lib_config(w)
+    inp = synth.prefill_inputs(w, 9, device="cuda", L=2000)
+    cache = ss.Cache(cfg, 4)
+    ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], cache)
+    twin = cache.clone()
+    dec = synth.decode_inputs(w, 9, 12, device="cuda", B=4)
+    ws = ss.decode_workspace(cfg, 4)
+    outs = []
+    for c in (cache, twin):
+        o = torch.empty(4, 32, 128, dtype=torch.bfloat16, device="cuda")
+        got = []
+        for t in range(12):
+            pos = torch.full((4,), 2000 + t, dtype=torch.int32, device="cuda")
+            ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], dec["v_new"][t], pos, c, o, ws=ws)
+            got.append(o.clone())
+        outs.append(torch.stack(got))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(cache.k, twin.k) and torch.equal(cache.v, twin.v)
+    assert torch.equal(cache.slot_pos, twin.slot_pos)
+    counters = ws[:4 * 8 * 4].view(torch.int32)
+    assert int(counters.abs().sum().item()) == 0
