@@ -109,7 +109,7 @@ def cpu_baseline(w, inp, dec, budget_s=12.0):
     cfg = oracle.Config(n_q_heads=w["n_q_heads"], n_kv_heads=w["n_kv_heads"], d_qk=w["d_qk"],
                         d_v=w["d_v"], L_sink=w["L_sink"], K=w["K"], L_recent=w["L_recent"],
                         W=w["W"], pool=w["pool"], v_aliases_k=w["v_aliases_k"],
-                        rope_theta=w["rope_theta"], rope_begin=w["rope_begin"],
+                        scale=w.get("scale", 0.0), rope_theta=w["rope_theta"], rope_begin=w["rope_begin"],
                         rope_end=w["rope_end"], dtype=w["dtype"])
     elem = 2 if w["dtype"] == "bf16" else 4
     pre_b, dec_b = algorithmic_bytes(dict(w, B=1), elem)
@@ -277,7 +277,8 @@ def main():
         "decode_step_us": round(1e6 * dec_call_s, 2),
         "prefill_compress_ms_per_layer": round(sum(pre_ms) / len(pre_ms), 4),
         "roofline": {
-            "kernel": "decode_kernel (RoPE + ring scatter + split-C flash-decode + merge)",
+            "kernel": ("decode_mla_kernel" if w["v_aliases_k"] else "decode_kernel")
+            + " (RoPE + ring scatter + split-C flash-decode + merge)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

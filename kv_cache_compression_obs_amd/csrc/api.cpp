@@ -12,7 +12,8 @@ constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool supported_shape(const ss_config* c) {
-  if (c->v_aliases_k) return false;  // the latent (MLA) kernels are not in this build yet
+  if (c->v_aliases_k)  // MLA absorbed latent: 512 value dims + 64 rotary dims, bf16
+    return c->dtype == SS_BF16 && c->d_qk == 576 && c->d_v == 512;
   if (c->dtype != SS_F32 && c->dtype != SS_BF16) return false;
   return (c->d_qk == 64 && c->d_v == 64) || (c->d_qk == 128 && c->d_v == 128);
 }
@@ -37,7 +38,7 @@ ss_status check_config(const ss_config* c) {
   if (C > (1LL << 30)) return SS_ERR_INVALID_ARG;
   if (c->dtype != SS_F32 && c->dtype != SS_BF16) return SS_ERR_INVALID_ARG;
   const int G = c->n_q_heads / c->n_kv_heads;
-  if (!supported_shape(c) || G > 16 || G * c->W > 128) return SS_ERR_UNSUPPORTED;
+  if (!supported_shape(c) || G > 16 || G * c->W > 256) return SS_ERR_UNSUPPORTED;
   if (c->rope_theta > 0.f && c->rope_end - c->rope_begin > 2 * ss::ROPE_MAX_PAIRS)
     return SS_ERR_UNSUPPORTED;
   return SS_OK;
@@ -99,20 +100,23 @@ DecodePlan plan_decode(const ss_config* c, int B_max) {
   // about DECODE_TARGET_WAVES waves when every slot is valid (short splits
   // balance rows of very different valid lengths).
   const long long tiles = (C + ss::DECODE_TILE - 1) / ss::DECODE_TILE;
-  long long want = (ss::DECODE_TARGET_WAVES + groups - 1) / groups;  // waves per group
-  if (want < 1) want = 1;
-  long long tpw = (tiles + want - 1) / want;
-  if (tpw > ss::DECODE_MAX_TILES) tpw = ss::DECODE_MAX_TILES;
-  if (tpw < 1) tpw = 1;
-  // the merge keeps G weights per split in the workgroup's V tiles (LDS)
-  const int G = c->n_q_heads / c->n_kv_heads;
-  const int es = c->dtype == SS_BF16 ? 2 : 4;
-  const long long max_splits = ss::decode_merge_capacity(c->d_v * es) / G;
-  const long long min_tpw =
-      (tiles + max_splits * ss::DECODE_WAVES - 1) / (max_splits * ss::DECODE_WAVES);
-  if (tpw < min_tpw) tpw = min_tpw;
-  p.wsplit = static_cast<int>(tpw) * ss::DECODE_TILE;
-  p.split = ss::DECODE_WAVES * p.wsplit;
+  if (c->v_aliases_k) {
+    // latent (MLA) kernel: the 4 waves of a workgroup share each tile; aim
+    // for 512 workgroups (2 per CU) with at most 64 tiles each
+    long long want_wg = (512 + groups - 1) / groups;
+    long long tpg = (tiles + want_wg - 1) / want_wg;
+    if (tpg > 64) tpg = 64;
+    if (tpg < 1) tpg = 1;
+    p.split = p.wsplit = static_cast<int>(tpg) * ss::DECODE_TILE;
+  } else {
+    long long want = (ss::DECODE_TARGET_WAVES + groups - 1) / groups;  // waves per group
+    if (want < 1) want = 1;
+    long long tpw = (tiles + want - 1) / want;
+    if (tpw > ss::DECODE_MAX_TILES) tpw = ss::DECODE_MAX_TILES;
+    if (tpw < 1) tpw = 1;
+    p.wsplit = static_cast<int>(tpw) * ss::DECODE_TILE;
+    p.split = ss::DECODE_WAVES * p.wsplit;
+  }
   p.n_split = (C + p.split - 1) / p.split;
   const size_t rows_q = static_cast<size_t>(B_max) * c->n_q_heads;
   size_t off = 0;

@@ -1,0 +1,141 @@
+// Helpers shared by the decode kernels (decode.hip, decode_mla.hip).
+#pragma once
+
+#include "common.h"
+#include "launch.h"
+
+namespace ss {
+namespace dec {
+
+// Rotate-half rotary embedding of element d of a row (value x, and xp = the
+// element it pairs with), computed in fp64 from the stored values and rounded
+// once to O (the cache dtype for keys, fp32 for queries).  cs/sn hold cos/sin
+// of the pair angles (pair i couples dims begin+i and begin+i+half).
+template <typename T, typename O>
+__device__ __forceinline__ O rotate_pair(T x, T xp, int d, bool rope, int begin, int half,
+                                         const double* cs, const double* sn) {
+  if (!rope || d < begin || d >= begin + 2 * half) return from_f32<O>(to_f32<T>(x));
+  const int i = d - begin;
+  const double v = to_f32<T>(x), w = to_f32<T>(xp);
+  if (i < half) return from_f64<O>(v * cs[i] - w * sn[i]);
+  return from_f64<O>(v * cs[i - half] + w * sn[i - half]);
+}
+
+// Device-scope stores: written through to the level shared by all XCDs (the
+// sc1 policy the compiler uses for agent-scope atomic stores), so publishing
+// them needs no whole-L2 write-back.  Completion is awaited with s_waitcnt.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev4(float* p, f32x4_t v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+
+// Operands of the P.V contraction.  The contraction index of lane group qg,
+// element i is the tile-local slot 4*i + qg (i < 8), which is exactly where
+// the Q.K^T accumulator left that slot's probability (see decode_kernel).
+template <typename T> struct PvOps;
+
+template <> struct PvOps<bf16_t> {
+  static constexpr int STEPS = 1;
+  static __device__ __forceinline__ bf16x8_t vfrag(const char* vt, int lrow, int db, int col,
+                                                   int qg, int) {
+    bf16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      e[i] = *reinterpret_cast<const bf16_t*>(vt + (4 * i + qg) * lrow + (16 * db + col) * 2);
+    return pack_bf16x8(e);
+  }
+};
+
+template <> struct PvOps<float> {
+  static constexpr int STEPS = 8;
+  static __device__ __forceinline__ float vfrag(const char* vt, int lrow, int db, int col, int qg,
+                                                int st) {
+    return *reinterpret_cast<const float*>(vt + (4 * st + qg) * lrow + (16 * db + col) * 4);
+  }
+};
+
+// fp32 values (the rotated query, the probabilities) as MFMA operands of the
+// storage type.  For bf16 each value becomes hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi): two MFMAs with exact bf16 x bf16 products carry x to
+// about 2^-17 relative, so only the cache itself is bf16.
+template <typename T> struct Split;
+
+template <> struct Split<float> {
+  static constexpr int N = 1;
+  static __device__ __forceinline__ void make(const float* v, float (&out)[1]) { out[0] = v[0]; }
+};
+
+template <> struct Split<bf16_t> {
+  static constexpr int N = 2;
+  static __device__ __forceinline__ void make(const float* v, bf16x8_t (&out)[2]) {
+    bf16_t hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = f32_to_bf16(v[e]);
+      lo[e] = f32_to_bf16(v[e] - bf16_to_f32(hi[e]));
+    }
+    out[0] = pack_bf16x8(hi);
+    out[1] = pack_bf16x8(lo);
+  }
+};
+
+
+// Orders LDS accesses of one wave (a wave executes its LDS instructions in
+// order; this keeps the compiler from moving them across the point).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The last workgroup of a (row, kv-head) group merges every split's partial
+// (max m_s, sum l_s, unnormalised o_s, written with st_dev/st_dev4):
+//   out[head, dv] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+// in split order.  Each thread loads every split's (m, l, o) of its 4
+// outputs at once (batches of MB splits): one memory round trip per batch.
+template <typename T, int DV>
+__device__ __forceinline__ void merge_splits(const DecodeArgs& a, size_t head0, int G, int ns,
+                                             int tid, int nthreads) {
+  constexpr int MB = 16;
+  for (int idx = tid; idx < G * (DV / 4); idx += nthreads) {
+    const int g = idx / (DV / 4), d4 = idx % (DV / 4);
+    const size_t base = (head0 + g) * a.n_split;
+    float M = -INFINITY, L = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < ns; sb += MB) {
+      float mv[MB], lv[MB];
+      f32x4_t ov[MB];
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const bool in = sb + j < ns;
+        const size_t s = base + sb + (in ? j : 0);
+        mv[j] = in ? a.part_ml[2 * s] : -INFINITY;
+        lv[j] = in ? a.part_ml[2 * s + 1] : 0.f;
+        ov[j] = in ? *reinterpret_cast<const f32x4_t*>(a.part_o + s * DV + 4 * d4)
+                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) Mn = fmaxf(Mn, mv[j]);
+      const float r = exp2f(M - Mn);
+      L *= r;
+      acc *= r;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const float w = exp2f(mv[j] - Mn);
+        L += w * lv[j];
+        acc += w * ov[j];
+      }
+      M = Mn;
+    }
+    const float inv = 1.f / L;
+    T* o = static_cast<T*>(a.out) + (head0 + g) * DV + 4 * d4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(acc[e] * inv);
+  }
+}
+
+}  // namespace dec
+}  // namespace ss

@@ -58,6 +58,8 @@ hipError_t launch_decode(int dtype, int D, int DV, int alias, const DecodeArgs& 
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStream_t st,
                                  hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_decode_mla(int dtype, int D, int DV, const DecodeArgs& a, hipStream_t st,
+                             hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t st);
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_gather(int dtype, int D, int DV, int alias, bool compressed,
@@ -76,13 +78,10 @@ constexpr int DECODE_WAVES = 4;   // waves per decode workgroup
 #endif
 constexpr int DECODE_TARGET_WAVES = SS_DECODE_TARGET_WAVES;
 constexpr int DECODE_MAX_TILES = SS_DECODE_MAX_TILES;
-// LDS row stride of the decode V tile (bytes) for value rows of `row_bytes`;
-// the workgroup's V tiles are reused for the merge weights, so a plan must
-// keep G * n_split <= decode_merge_capacity().
+// LDS row stride of the decode V tile (bytes) for value rows of `row_bytes`
+// (+32 B keeps the transposed 16-bit reads of the 4 lane groups on disjoint
+// banks).
 constexpr int decode_vrow_stride(int row_bytes) { return row_bytes + 32; }
-constexpr int decode_merge_capacity(int row_bytes) {
-  return DECODE_WAVES * DECODE_TILE * decode_vrow_stride(row_bytes) / 4;
-}
 constexpr int SCORE_KT_MAX = 64;  // keys per score tile (chunks are multiples of it)
 
 }  // namespace ss

@@ -23,35 +23,35 @@ namespace ss {
 
 namespace {
 
-constexpr int SW = 8;          // waves per score workgroup (one 16-row block each)
-constexpr int SNT = SW * 64;   // threads per score workgroup
-
-template <typename T, int D, int KT>
+// A key tile of KT rows staged in LDS by the NT threads of a score workgroup.
+template <typename T, int D, int KT, int NT>
 struct KeyTile {
   static constexpr int ES = static_cast<int>(sizeof(T));
   static constexpr int KROW = D * ES;      // bytes of one key row
   static constexpr int LROW = KROW + 16;   // LDS row stride (bytes)
   static constexpr int KCH = KROW / 16;    // 16-byte chunks per row
-  static constexpr int NLD = KT * KCH / SNT;
+  static constexpr int NLD = cdiv(KT * KCH, NT);
   static constexpr int BYTES = KT * LROW;
-  static_assert((KT * KCH) % SNT == 0, "tile must split evenly over the workgroup");
 
   // rows t0 .. t0+KT-1 of kbase (clamped to kend-1) into registers
   static __device__ __forceinline__ void load(u32x4_t (&r)[NLD], const T* kbase, int t0, int kend,
                                               int tid) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int id = i * SNT + tid;
-      const int key = min(t0 + id / KCH, kend - 1);
-      r[i] = *reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const char*>(kbase + static_cast<size_t>(key) * D) + (id % KCH) * 16);
+      const int id = i * NT + tid;
+      if (id < KT * KCH) {
+        const int key = min(t0 + id / KCH, kend - 1);
+        r[i] = *reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const char*>(kbase + static_cast<size_t>(key) * D) + (id % KCH) * 16);
+      }
     }
   }
   static __device__ __forceinline__ void store(char* buf, const u32x4_t (&r)[NLD], int tid) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int id = i * SNT + tid;
-      *reinterpret_cast<u32x4_t*>(buf + (id / KCH) * LROW + (id % KCH) * 16) = r[i];
+      const int id = i * NT + tid;
+      if (id < KT * KCH)
+        *reinterpret_cast<u32x4_t*>(buf + (id / KCH) * LROW + (id % KCH) * 16) = r[i];
     }
   }
   // B operand (K^T) fragment: lane (col, qg) takes key 16*kb + col, dims
@@ -77,14 +77,14 @@ __device__ __forceinline__ void load_q(typename Mma<T>::frag (&qf)[D / Mma<T>::K
                : Mma<T>::zero();
 }
 
-// Pass 1.  Grid (n_chunk1, Hkv, b).  Wave w owns rows 16w .. 16w+15 of the
-// group; accumulator lane (col, qg) register r holds row 16w + 4qg + r and key
-// 16kb + col of the tile.  Each lane keeps running (max, sum) of its rows
-// over the keys it sees; the 16 lanes of a row are merged at the end.
-template <typename T, int D, int KT>
-__global__ __launch_bounds__(SNT) void score_rowstat_kernel(PrefillArgs a) {
+// Pass 1.  Grid (n_chunk1, Hkv, b), NWV waves.  Wave w owns rows 16w .. 16w+15
+// of the group; accumulator lane (col, qg) register r holds row 16w + 4qg + r
+// and key 16kb + col of the tile.  Each lane keeps running (max, sum) of its
+// rows over the keys it sees; the 16 lanes of a row are merged at the end.
+template <typename T, int D, int KT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) {
   using MM = Mma<T>;
-  using KTile = KeyTile<T, D, KT>;
+  using KTile = KeyTile<T, D, KT, 64 * NWV>;
   constexpr int NC = D / MM::KSTEP;
   constexpr int NKB = KT / 16;
   __shared__ __attribute__((aligned(16))) char lds[2 * KTile::BYTES];
@@ -192,15 +192,15 @@ __global__ __launch_bounds__(256) void score_rowstat_combine_kernel(PrefillArgs 
 // Pass 2.  Grid (n_chunk2, Hkv, b) over the middle keys [S, L-R).  Every
 // middle key is visible to every observation row (the window lies inside the
 // recent region), so no causal mask.  Column sums: 4 rows in registers, then
-// the 4 lane groups (xor 16, 32), then the 8 waves through LDS in wave order.
-template <typename T, int D, int KT>
-__global__ __launch_bounds__(SNT) void score_columns_kernel(PrefillArgs a) {
+// the 4 lane groups (xor 16, 32), then the NWV waves through LDS in wave order.
+template <typename T, int D, int KT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) {
   using MM = Mma<T>;
-  using KTile = KeyTile<T, D, KT>;
+  using KTile = KeyTile<T, D, KT, 64 * NWV>;
   constexpr int NC = D / MM::KSTEP;
   constexpr int NKB = KT / 16;
   __shared__ __attribute__((aligned(16))) char lds[2 * KTile::BYTES];
-  __shared__ float red[2][SW][KT];
+  __shared__ float red[2][NWV][KT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, qg = lane >> 4;
@@ -321,16 +321,24 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
   }
 }
 
-template <typename T, int D, int KT>
-hipError_t run_scores(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+template <typename T, int D, int KT, int NWV>
+hipError_t run_scores_w(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
-  score_rowstat_kernel<T, D, KT><<<dim3(a.n_chunk1, a.Hkv, a.b), SNT, 0, st>>>(a);
+  score_rowstat_kernel<T, D, KT, NWV><<<dim3(a.n_chunk1, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
   const size_t rows = static_cast<size_t>(a.b) * a.Hkv * a.Rg;
   score_rowstat_combine_kernel<<<static_cast<unsigned>(cdiv(static_cast<int>(rows), 256)), 256, 0,
                                  st>>>(a);
-  score_columns_kernel<T, D, KT><<<dim3(a.n_chunk2, a.Hkv, a.b), SNT, 0, st>>>(a);
+  score_columns_kernel<T, D, KT, NWV><<<dim3(a.n_chunk2, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+// One 16-row block per wave: 8 waves cover G*W <= 128 rows, 16 waves <= 256.
+template <typename T, int D, int KT>
+hipError_t run_scores(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.Rg <= 128) return run_scores_w<T, D, KT, 8>(a, st, ev0, ev1);
+  if (a.Rg <= 256) return run_scores_w<T, D, KT, 16>(a, st, ev0, ev1);
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D, int DV, bool ALIAS>
@@ -347,12 +355,17 @@ hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStre
   if (dtype == 0 && D == 128) return run_scores<float, 128, 64>(a, st, ev0, ev1);
   if (dtype == 1 && D == 64) return run_scores<bf16_t, 64, 64>(a, st, ev0, ev1);
   if (dtype == 1 && D == 128) return run_scores<bf16_t, 128, 64>(a, st, ev0, ev1);
+  if (dtype == 1 && D == 576) return run_scores_w<bf16_t, 576, 32, 16>(a, st, ev0, ev1);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_gather(int dtype, int D, int DV, int alias, bool compressed,
                                  const PrefillArgs& a, hipStream_t st) {
-  if (alias) return hipErrorInvalidValue;
+  if (alias) {
+    if (dtype == 1 && D == 576 && DV == 512)
+      return run_gather<bf16_t, 576, 512, true>(compressed, a, st);
+    return hipErrorInvalidValue;
+  }
   if (dtype == 0 && D == 64 && DV == 64) return run_gather<float, 64, 64, false>(compressed, a, st);
   if (dtype == 0 && D == 128 && DV == 128)
     return run_gather<float, 128, 128, false>(compressed, a, st);

@@ -18,7 +18,9 @@ page's configured L_recent = 31,744):
                       (64+960+31744), W=32, pool 7, 32 layers, 512 steps
   deepseek_mla_128k   32 x (8q/1 latent) x d576 (value = first 512), bf16,
                       prompt 131072 -> C=32768, W=32, pool 7, rope 1e4 on
-                      dims 512..575, 61 layers, 512 steps
+                      dims 512..575, softmax scale 1/sqrt(192) (the model's
+                      per-head 128 + 64 query dims before absorption),
+                      61 layers, 512 steps
   llama8b_cb64        64 rows x (32q/8kv) x d128, bf16, C=32768, request
                       lengths log-uniform in [1k, 128k], 1000 steps
 """
@@ -27,7 +29,11 @@ from __future__ import annotations
 import copy
 import math
 
+import numpy as np
 import torch
+
+# 1/sqrt(128 + 64) held exactly as the fp32 value the library receives
+MLA_SCALE = float(np.float32(1.0 / math.sqrt(192.0)))
 
 WORKLOADS = {
     "tiny_fp32": dict(
@@ -47,7 +53,7 @@ WORKLOADS = {
         heavy_keys=0, heavy_scale=1.0, key_lognormal=True),
     "deepseek_mla_128k": dict(
         B=32, n_q_heads=8, n_kv_heads=1, d_qk=576, d_v=512, v_aliases_k=True,
-        L=131072, L_sink=64, K=960, L_recent=31744, W=32, pool=7, dtype="bf16",
+        scale=MLA_SCALE, L=131072, L_sink=64, K=960, L_recent=31744, W=32, pool=7, dtype="bf16",
         rope_theta=10000.0, rope_begin=512, rope_end=576, steps=512, layers=61,
         heavy_keys=0, heavy_scale=1.0, key_lognormal=False),
     "llama8b_cb64": dict(

@@ -27,7 +27,7 @@ def oracle_config(w: dict) -> oracle.Config:
     return oracle.Config(
         n_q_heads=w["n_q_heads"], n_kv_heads=w["n_kv_heads"], d_qk=w["d_qk"], d_v=w["d_v"],
         L_sink=w["L_sink"], K=w["K"], L_recent=w["L_recent"], W=w["W"], pool=w["pool"],
-        v_aliases_k=w["v_aliases_k"], rope_theta=w["rope_theta"], rope_begin=w["rope_begin"],
+        v_aliases_k=w["v_aliases_k"], scale=w.get("scale", 0.0), rope_theta=w["rope_theta"], rope_begin=w["rope_begin"],
         rope_end=w["rope_end"], dtype=w["dtype"])
 
 
@@ -107,3 +107,119 @@ def upload_oracle_state(state: "oracle.CacheState", cache):
         cache.v.copy_(torch.from_numpy(state.v).to(dt))
     cache.slot_pos.copy_(torch.from_numpy(state.slot_pos).to(torch.int32))
     cache.n_tokens.copy_(torch.from_numpy(state.n_tokens).to(torch.int32))
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check_prefill_group(w, inp, res_lib, bi, h, row=None, raw_rtol=2e-5):
+    cache, raw, pooled, sel = res_lib
+    row = bi if row is None else row
+    S, K, R, C = w["L_sink"], w["K"], w["L_recent"], w["C"]
+    L = inp["k"].shape[2]
+    ref = oracle_prefill_group(w, inp, bi, h)
+    sp = cache.slot_pos[row, h].cpu().numpy().astype(np.int64)
+    stats = {}
+    if L > C:
+        # scores: relative to the group's largest score (small scores carry
+        # absolute fp32 rounding of the probabilities)
+        scale = ref.raw[0].max()
+        err = np.abs(raw[bi, h] - ref.raw[0]).max() / scale
+        assert err <= raw_rtol, f"raw scores rel err {err:.3g}"
+        np.testing.assert_array_equal(pooled[bi, h], pool_exact(raw[bi, h], w["pool"]))
+        n_band, swaps = compare_selection(sel[bi, h], ref.pooled[0], ref.sel[0], K)
+        stats = dict(raw_err=err, band=n_band, swaps=swaps)
+        np.testing.assert_array_equal(sp[:S], ref.slot_pos[0, :S])
+        np.testing.assert_array_equal(sp[S + K:], ref.slot_pos[0, S + K:])
+        np.testing.assert_array_equal(sp[S:S + K], S + sel[bi, h])
+    else:
+        np.testing.assert_array_equal(sp, ref.slot_pos[0])
+    # every valid slot holds a bit-exact copy of the input row it names
+    n = min(L, C)
+    k_in = inp["k"][bi, h]
+    kc = cache.k[row, h, :n].cpu()
+    assert torch.equal(kc, k_in[torch.from_numpy(sp[:n])].cpu())
+    if cache.v is not None:
+        assert torch.equal(cache.v[row, h, :n].cpu(), inp["v"][bi, h][torch.from_numpy(sp[:n])].cpu())
+    assert int(cache.n_tokens[row].item()) == L
+    return stats
+
+
+def pool_exact(x, P):
+    p = (P - 1) // 2
+    m = len(x)
+    pad = np.concatenate([np.full(p, -np.inf, np.float32), x, np.full(p, -np.inf, np.float32)])
+    return np.lib.stride_tricks.sliding_window_view(pad, P).max(axis=1)
+
+
+def prefill_case(w, seed, B=None, L=None, groups=None, device="cuda", raw_rtol=2e-5):
+    say(f"prefill {w['name']} dtype={w['dtype']} d={w['d_qk']} B={B or w['B']} L={L or w['L']}")
+    inp = synth.prefill_inputs(w, seed, device=device, B=B, L=L)
+    if device != "cuda":
+        inp = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    res = run_lib_prefill(w, inp)
+    Bn, Hkv = inp["k"].shape[0], inp["k"].shape[1]
+    groups = groups or [(b, h) for b in range(Bn) for h in range(Hkv)]
+    worst = {}
+    for bi, h in groups:
+        st = check_prefill_group(w, inp, res, bi, h, raw_rtol=raw_rtol)
+        for k_, v_ in st.items():
+            worst[k_] = max(worst.get(k_, 0), v_)
+    say(f"  {worst}")
+    return worst
+
+
+def decode_case(w, L, steps, seed, B=None, positions=None, check_every=1):
+    """positions: optional fn(t) -> np.array of per-row pos (default L + t)."""
+    cfg_o, cfg_l = oracle_config(w), lib_config(w)
+    inp = synth.prefill_inputs(w, seed, device="cpu", B=B, L=L)
+    B = inp["k"].shape[0]
+    state = oracle.CacheState(cfg_o, B)
+    for bi in range(B):
+        state.admit(bi, oracle_prefill_request(w, inp, bi))
+    cache = ss.Cache(cfg_l, B)
+    upload_oracle_state(state, cache)
+    dec = synth.decode_inputs(w, seed, steps, B=B)
+    dt = synth.TORCH_DTYPE[w["dtype"]]
+    out = torch.empty(B, w["n_q_heads"], w["d_v"], dtype=dt, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # an uninitialised workspace made ready by the library's own init call
+    ws = torch.full((ss.ss_decode_workspace_bytes(cfg_l, B),), 0xA5, dtype=torch.uint8,
+                    device="cuda")
+    ss.ss_decode_workspace_init(cfg_l, B, ws)
+    tol = OUT_TOL[w["dtype"]]
+    worst = 0.0
+    for t in range(steps):
+        pos_np = positions(t) if positions else np.full(B, L + t)
+        pos = torch.from_numpy(np.asarray(pos_np, dtype=np.int32)).cuda()
+        q, kn = dec["q"][t].cuda(), dec["k_new"][t].cuda()
+        vn = dec["v_new"][t].cuda() if dec["v_new"] is not None else None
+        err.zero_()
+        ss.ss_decode_step(cfg_l, q, kn, vn, pos, cache, out, err, ws)
+        ref, ref_err = oracle.decode_step(
+            state, synth.to_f64(dec["q"][t]), synth.to_f64(dec["k_new"][t]),
+            synth.to_f64(dec["v_new"][t]) if dec["v_new"] is not None else None, pos_np)
+        torch.cuda.synchronize()
+        if t % check_every and t != steps - 1:
+            continue
+        got = out.float().cpu().numpy().astype(np.float64)
+        diff = np.abs(got - ref).max()
+        worst = max(worst, diff)
+        assert diff <= tol, f"step {t}: max-abs {diff:.3g} > {tol}"
+        assert bool(err.item()) == bool(ref_err), f"step {t}: err flag"
+        np.testing.assert_array_equal(cache.n_tokens.cpu().numpy(), state.n_tokens)
+        for b in range(B):
+            p = int(pos_np[b])
+            if p < 0:
+                continue
+            slot = oracle.ring_slot(p, w["L_sink"], w["K"], w["L_recent"])
+            np.testing.assert_array_equal(cache.slot_pos[b, :, slot].cpu().numpy(),
+                                          state.slot_pos[b, :, slot])
+            np.testing.assert_array_equal(cache.k[b, :, slot].double().cpu().numpy(),
+                                          state.k[b, :, slot])
+            if cache.v is not None:
+                np.testing.assert_array_equal(cache.v[b, :, slot].double().cpu().numpy(),
+                                              state.v[b, :, slot])
+    np.testing.assert_array_equal(cache.slot_pos.cpu().numpy(), state.slot_pos)
+    return worst

@@ -72,6 +72,40 @@ def test_invalid_config_is_rejected_before_launch(bad, code):
     assert ss.ss_decode_workspace_bytes(cfg, 4) == 0
 
 
+def _mla(**kw):
+    base = dict(n_q_heads=8, n_kv_heads=1, d_qk=576, d_v=512, v_aliases_k=True, L_sink=64,
+                K=960, L_recent=31744, W=32, pool=7, dtype="bf16", rope_theta=1e4,
+                rope_begin=512, rope_end=576)
+    base.update(kw)
+    return ss.make_config(**base)
+
+
+def test_mla_latent_config_is_accepted():
+    cfg = _mla()
+    assert ss.ss_cache_slots(cfg) == 32768
+    # partial outputs of 512 value dims per head and split
+    assert ss.ss_decode_workspace_bytes(cfg, 32) >= 32 * 8 * 512 * 4
+    assert ss.ss_prefill_workspace_bytes(cfg, 32, 131072) > 32 * (131072 - 32768) * 4 * 2
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(dtype="f32"), ss.SS_ERR_UNSUPPORTED),          # latent kernels are bf16 only
+    (dict(d_v=256), ss.SS_ERR_UNSUPPORTED),
+    (dict(d_qk=128, d_v=128, rope_begin=0, rope_end=128), ss.SS_ERR_UNSUPPORTED),
+    (dict(d_v=640), ss.SS_ERR_INVALID_ARG),              # value longer than the latent
+    (dict(v_aliases_k=False), ss.SS_ERR_UNSUPPORTED),    # a separate 512-dim value cache
+    (dict(n_q_heads=32), ss.SS_ERR_UNSUPPORTED),         # G * W = 1024 score rows
+])
+def test_mla_unsupported_shapes_are_rejected(bad, code):
+    cfg = _mla(**bad)
+    assert ss.ss_decode_workspace_bytes(cfg, 4) == 0
+    lib = ss.lib()
+    cache = ss.ss_cache(None, None, None, None, 1)
+    st = lib.ss_decode_step(ctypes.byref(cfg), None, None, None, None, ctypes.byref(cache), None,
+                            None, None, 0, None)
+    assert st == code
+
+
 def test_null_pointers_and_small_workspace_are_rejected():
     cfg = _cfg()
     lib = ss.lib()

@@ -8,110 +8,50 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from kv_cache_compression_obs_amd import snapstream as ss
 from kv_cache_compression_obs_amd import synth
-from parity import OUT_TOL, lib_config, oracle_config, oracle_prefill_request, upload_oracle_state
+from parity import decode_case, lib_config, say
 
 pytestmark = pytest.mark.gpu
 
 
-def _say(msg):
-    print(msg, flush=True)
-
-
-def _decode_case(w, L, steps, seed, B=None, positions=None, check_every=1):
-    """positions: optional fn(t) -> np.array of per-row pos (default L + t)."""
-    cfg_o, cfg_l = oracle_config(w), lib_config(w)
-    inp = synth.prefill_inputs(w, seed, device="cpu", B=B, L=L)
-    B = inp["k"].shape[0]
-    state = oracle.CacheState(cfg_o, B)
-    for bi in range(B):
-        state.admit(bi, oracle_prefill_request(w, inp, bi))
-    cache = ss.Cache(cfg_l, B)
-    upload_oracle_state(state, cache)
-    dec = synth.decode_inputs(w, seed, steps, B=B)
-    dt = synth.TORCH_DTYPE[w["dtype"]]
-    out = torch.empty(B, w["n_q_heads"], w["d_v"], dtype=dt, device="cuda")
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    # an uninitialised workspace made ready by the library's own init call
-    ws = torch.full((ss.ss_decode_workspace_bytes(cfg_l, B),), 0xA5, dtype=torch.uint8,
-                    device="cuda")
-    ss.ss_decode_workspace_init(cfg_l, B, ws)
-    tol = OUT_TOL[w["dtype"]]
-    worst = 0.0
-    for t in range(steps):
-        pos_np = positions(t) if positions else np.full(B, L + t)
-        pos = torch.from_numpy(np.asarray(pos_np, dtype=np.int32)).cuda()
-        q, kn = dec["q"][t].cuda(), dec["k_new"][t].cuda()
-        vn = dec["v_new"][t].cuda() if dec["v_new"] is not None else None
-        err.zero_()
-        ss.ss_decode_step(cfg_l, q, kn, vn, pos, cache, out, err, ws)
-        ref, ref_err = oracle.decode_step(
-            state, synth.to_f64(dec["q"][t]), synth.to_f64(dec["k_new"][t]),
-            synth.to_f64(dec["v_new"][t]) if dec["v_new"] is not None else None, pos_np)
-        torch.cuda.synchronize()
-        if t % check_every and t != steps - 1:
-            continue
-        got = out.float().cpu().numpy().astype(np.float64)
-        diff = np.abs(got - ref).max()
-        worst = max(worst, diff)
-        assert diff <= tol, f"step {t}: max-abs {diff:.3g} > {tol}"
-        assert bool(err.item()) == bool(ref_err), f"step {t}: err flag"
-        np.testing.assert_array_equal(cache.n_tokens.cpu().numpy(), state.n_tokens)
-        for b in range(B):
-            p = int(pos_np[b])
-            if p < 0:
-                continue
-            slot = oracle.ring_slot(p, w["L_sink"], w["K"], w["L_recent"])
-            np.testing.assert_array_equal(cache.slot_pos[b, :, slot].cpu().numpy(),
-                                          state.slot_pos[b, :, slot])
-            np.testing.assert_array_equal(cache.k[b, :, slot].double().cpu().numpy(),
-                                          state.k[b, :, slot])
-            if cache.v is not None:
-                np.testing.assert_array_equal(cache.v[b, :, slot].double().cpu().numpy(),
-                                              state.v[b, :, slot])
-    np.testing.assert_array_equal(cache.slot_pos.cpu().numpy(), state.slot_pos)
-    return worst
-
-
 def test_decode_tiny_fp32_after_compression():
     w = synth.workload("tiny_fp32")
-    _say("decode tiny_fp32 L=512 steps=64")
-    _decode_case(w, L=512, steps=64, seed=1)
+    say("decode tiny_fp32 L=512 steps=64")
+    decode_case(w, L=512, steps=64, seed=1)
 
 
 def test_decode_tiny_fp32_ring_wraps():
     w = synth.workload("tiny_fp32")
-    _say("decode tiny_fp32 L=512 steps=300 (ring index wraps)")
-    _decode_case(w, L=512, steps=300, seed=2, check_every=7)
+    say("decode tiny_fp32 L=512 steps=300 (ring index wraps)")
+    decode_case(w, L=512, steps=300, seed=2, check_every=7)
 
 
 def test_decode_tiny_fp32_short_prompt_crosses_capacity():
     # uncompressed prompt of 100 tokens; the valid prefix grows through n = C
     w = synth.workload("tiny_fp32")
-    _say("decode tiny_fp32 L=100 steps=160")
-    _decode_case(w, L=100, steps=160, seed=3, check_every=3)
+    say("decode tiny_fp32 L=100 steps=160")
+    decode_case(w, L=100, steps=160, seed=3, check_every=3)
 
 
 def test_decode_empty_prompt_single_slot():
     w = synth.workload("tiny_fp32")
-    _say("decode tiny_fp32 L=1 steps=3")
-    _decode_case(w, L=1, steps=3, seed=4)
+    say("decode tiny_fp32 L=1 steps=3")
+    decode_case(w, L=1, steps=3, seed=4)
 
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_bf16_rope_ring(d):
     w = synth.workload("llama8b_c4k", B=3, d_qk=d, d_v=d, rope_end=d, L_sink=4, K=28,
                        L_recent=64)
-    _say(f"decode bf16 d={d} C=96 L=200 steps=150")
-    _decode_case(w, L=200, steps=150, seed=5, check_every=5)
+    say(f"decode bf16 d={d} C=96 L=200 steps=150")
+    decode_case(w, L=200, steps=150, seed=5, check_every=5)
 
 
 def test_decode_fp32_d128_rope():
     w = synth.workload("llama8b_c4k", B=2, dtype="f32", L_sink=4, K=28, L_recent=64)
-    _say("decode f32 d=128 C=96 L=300 steps=70")
-    _decode_case(w, L=300, steps=70, seed=6, check_every=3)
+    say("decode f32 d=128 C=96 L=300 steps=70")
+    decode_case(w, L=300, steps=70, seed=6, check_every=3)
 
 
 def test_decode_mixed_rows_inactive_and_mismatch():
@@ -134,17 +74,17 @@ def test_decode_mixed_rows_inactive_and_mismatch():
             p[3] = L + t + 3
         return p
 
-    _say("decode mixed rows")
-    _decode_case(w, L=L, steps=20, seed=7, positions=positions)
+    say("decode mixed rows")
+    decode_case(w, L=L, steps=20, seed=7, positions=positions)
 
 
 def test_decode_llama8b_c4k_full_shape():
     # 16 rows x 8 kv-heads x C=4096 (bf16, rope 5e5): the benchmark's decode
     # launch configuration; oracle compares every output of 3 steps
     w = synth.workload("llama8b_c4k")
-    _say("decode llama8b_c4k full B=16 L=16384 steps=3")
-    worst = _decode_case(w, L=w["L"], steps=3, seed=8)
-    _say(f"  worst max-abs {worst:.3g}")
+    say("decode llama8b_c4k full B=16 L=16384 steps=3")
+    worst = decode_case(w, L=w["L"], steps=3, seed=8)
+    say(f"  worst max-abs {worst:.3g}")
 
 
 def test_decode_is_deterministic_and_workspace_reusable():

@@ -1,0 +1,105 @@
+"""GPU parity of the absorbed multi-head latent attention (MLA) variant against
+the fp64 oracle: 8 q-heads share one cached 576-dim latent row whose first 512
+dims are the value; rotary embedding covers dims 512..575 (theta 1e4).
+
+Prefill: the observation-window scores over 576-dim keys (256 score rows per
+group), pooling, selection and the gather of latent rows.  Decode: RoPE on the
+rotary dims, the ring scatter of the latent row, attention with value = the
+row's first 512 dims, and the split merge."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_obs_amd import snapstream as ss
+from kv_cache_compression_obs_amd import synth
+from parity import (OUT_TOL, decode_case, lib_config, oracle_config, oracle_prefill_request,
+                    prefill_case, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _mla(**kw):
+    return synth.workload("deepseek_mla_128k", **kw)
+
+
+def test_mla_prefill_small_ragged():
+    # L = 4999: 3 row-stat chunks (2048) with a ragged tail; m = 4999 - 16 - 512
+    # = 4471 middle keys (column chunks of 1024, last tile of 55 keys)
+    prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512), 21, L=4999)
+
+
+def test_mla_prefill_uncompressed_is_identity():
+    prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512), 22, L=700)
+
+
+def test_mla_prefill_full_shape_sampled_groups():
+    # 32 requests, 131072 -> 32768 latent rows on the GPU; the oracle checks
+    # three requests one by one
+    prefill_case(_mla(), 23, groups=[(0, 0), (17, 0), (31, 0)])
+
+
+def test_mla_decode_ring():
+    say("decode mla C=96 L=200 steps=150")
+    decode_case(_mla(B=3, L_sink=4, K=28, L_recent=64), L=200, steps=150, seed=24, check_every=5)
+
+
+def test_mla_decode_short_prompt_crosses_capacity():
+    say("decode mla C=96 L=50 steps=80")
+    decode_case(_mla(B=2, L_sink=4, K=28, L_recent=64), L=50, steps=80, seed=25, check_every=3)
+
+
+def test_mla_decode_many_splits():
+    # C = 2048: 64 splits of one tile per row, merged in 4 batches
+    say("decode mla C=2048 L=3000 steps=4")
+    decode_case(_mla(B=2, L_sink=16, K=1008, L_recent=1024), L=3000, steps=4, seed=26)
+
+
+def test_mla_decode_mixed_rows():
+    # row 1 inactive for the first steps, row 2 skips ahead (error flag)
+    L = 150
+
+    def positions(t):
+        p = np.array([L + t, L + t - 4 if t >= 4 else -1, L + t + (5 if t >= 6 else 0)])
+        return p
+
+    say("decode mla mixed rows")
+    decode_case(_mla(B=3, L_sink=4, K=28, L_recent=64), L=L, steps=12, seed=27,
+                positions=positions)
+
+
+def test_mla_decode_full_shape_sampled_rows():
+    # 32 rows x C=32768 latent slots, every slot valid (prompt of exactly C
+    # tokens, so prefill is a copy on both sides); decode wraps into the ring.
+    # The library steps all rows; the oracle follows rows 0, 13 and 31.
+    w = _mla()
+    C, B, steps, rows = w["C"], w["B"], 2, [0, 13, 31]
+    cfg_l = lib_config(w)
+    inp = synth.prefill_inputs(w, 28, device="cuda", L=C)
+    cache = ss.Cache(cfg_l, B)
+    ss.ss_prefill_compress(cfg_l, inp["q_obs"], inp["k"], None, cache)
+    state = oracle.CacheState(oracle_config(w), len(rows))
+    for i, r in enumerate(rows):
+        state.admit(i, oracle_prefill_request(w, inp, r))
+    del inp
+    dec = synth.decode_inputs(w, 28, steps, device="cuda", B=B)
+    out = torch.empty(B, w["n_q_heads"], w["d_v"], dtype=torch.bfloat16, device="cuda")
+    ws = ss.decode_workspace(cfg_l, B)
+    for t in range(steps):
+        say(f"decode mla full B=32 C=32768 step {t}")
+        pos_np = np.full(B, C + t)
+        pos = torch.from_numpy(pos_np.astype(np.int32)).cuda()
+        ss.ss_decode_step(cfg_l, dec["q"][t], dec["k_new"][t], None, pos, cache, out, ws=ws)
+        ref, _ = oracle.decode_step(state, synth.to_f64(dec["q"][t][rows]),
+                                    synth.to_f64(dec["k_new"][t][rows]), None, pos_np[rows])
+        torch.cuda.synchronize()
+        got = out[rows].double().cpu().numpy()
+        diff = np.abs(got - ref).max()
+        say(f"  max-abs {diff:.3g}")
+        assert diff <= OUT_TOL["bf16"], f"step {t}: max-abs {diff:.3g}"
+        slot = oracle.ring_slot(C + t, w["L_sink"], w["K"], w["L_recent"])
+        for i, r in enumerate(rows):
+            np.testing.assert_array_equal(cache.k[r, :, slot].double().cpu().numpy(),
+                                          state.k[i, :, slot])
+            assert int(cache.slot_pos[r, 0, slot].item()) == C + t
+    assert (cache.n_tokens == C + steps).all()

@@ -4,85 +4,23 @@ Checked per (request, kv-head): middle scores (relative error), pooled
 scores, the selection under the tie-band rule, the sink and ring slot maps
 (exact), the middle slot map (as a set, same rule), every cache row a
 bit-exact copy of the input row its slot names, n_tokens."""
-import numpy as np
 import pytest
 import torch
 
 from kv_cache_compression_obs_amd import synth
-from parity import compare_selection, oracle_prefill_group, run_lib_prefill
+from parity import check_prefill_group, prefill_case, run_lib_prefill, say
 
 pytestmark = pytest.mark.gpu
 
 
-def _say(msg):
-    print(msg, flush=True)
-
-
-def _check_group(w, inp, res_lib, bi, h, row=None, raw_rtol=2e-5):
-    cache, raw, pooled, sel = res_lib
-    row = bi if row is None else row
-    S, K, R, C = w["L_sink"], w["K"], w["L_recent"], w["C"]
-    L = inp["k"].shape[2]
-    ref = oracle_prefill_group(w, inp, bi, h)
-    sp = cache.slot_pos[row, h].cpu().numpy().astype(np.int64)
-    stats = {}
-    if L > C:
-        # scores: relative to the group's largest score (small scores carry
-        # absolute fp32 rounding of the probabilities)
-        scale = ref.raw[0].max()
-        err = np.abs(raw[bi, h] - ref.raw[0]).max() / scale
-        assert err <= raw_rtol, f"raw scores rel err {err:.3g}"
-        np.testing.assert_array_equal(pooled[bi, h], _pool_exact(raw[bi, h], w["pool"]))
-        n_band, swaps = compare_selection(sel[bi, h], ref.pooled[0], ref.sel[0], K)
-        stats = dict(raw_err=err, band=n_band, swaps=swaps)
-        np.testing.assert_array_equal(sp[:S], ref.slot_pos[0, :S])
-        np.testing.assert_array_equal(sp[S + K:], ref.slot_pos[0, S + K:])
-        np.testing.assert_array_equal(sp[S:S + K], S + sel[bi, h])
-    else:
-        np.testing.assert_array_equal(sp, ref.slot_pos[0])
-    # every valid slot holds a bit-exact copy of the input row it names
-    n = min(L, C)
-    k_in = inp["k"][bi, h]
-    kc = cache.k[row, h, :n].cpu()
-    assert torch.equal(kc, k_in[torch.from_numpy(sp[:n])].cpu())
-    if cache.v is not None:
-        assert torch.equal(cache.v[row, h, :n].cpu(), inp["v"][bi, h][torch.from_numpy(sp[:n])].cpu())
-    assert int(cache.n_tokens[row].item()) == L
-    return stats
-
-
-def _pool_exact(x, P):
-    p = (P - 1) // 2
-    m = len(x)
-    pad = np.concatenate([np.full(p, -np.inf, np.float32), x, np.full(p, -np.inf, np.float32)])
-    return np.lib.stride_tricks.sliding_window_view(pad, P).max(axis=1)
-
-
-def _case(w, seed, B=None, L=None, groups=None, device="cuda", raw_rtol=2e-5):
-    _say(f"prefill {w['name']} dtype={w['dtype']} d={w['d_qk']} B={B or w['B']} L={L or w['L']}")
-    inp = synth.prefill_inputs(w, seed, device=device, B=B, L=L)
-    if device != "cuda":
-        inp = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
-    res = run_lib_prefill(w, inp)
-    Bn, Hkv = inp["k"].shape[0], inp["k"].shape[1]
-    groups = groups or [(b, h) for b in range(Bn) for h in range(Hkv)]
-    worst = {}
-    for bi, h in groups:
-        st = _check_group(w, inp, res, bi, h, raw_rtol=raw_rtol)
-        for k_, v_ in st.items():
-            worst[k_] = max(worst.get(k_, 0), v_)
-    _say(f"  {worst}")
-    return worst
-
-
 @pytest.mark.parametrize("seed", [1, 2])
 def test_prefill_tiny_fp32(seed):
-    _case(synth.workload("tiny_fp32"), seed)
+    prefill_case(synth.workload("tiny_fp32"), seed)
 
 
 @pytest.mark.parametrize("L", [1, 100, 196])
 def test_prefill_uncompressed_is_identity(L):
-    _case(synth.workload("tiny_fp32"), 3, L=L)
+    prefill_case(synth.workload("tiny_fp32"), 3, L=L)
 
 
 @pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "bf16"), (128, "f32")])
@@ -91,7 +29,7 @@ def test_prefill_small_ragged(d, dtype):
     # m = 4999 - 16 - 512 = 4471 (chunk2 1024, tile 64 -> tail 55)
     w = synth.workload("llama8b_c4k", B=2, d_qk=d, d_v=d, rope_end=d, dtype=dtype, L_sink=16,
                        K=200, L_recent=512)
-    _case(w, 4, L=4999)
+    prefill_case(w, 4, L=4999)
 
 
 def test_prefill_admits_into_chosen_rows():
@@ -104,16 +42,16 @@ def test_prefill_admits_into_chosen_rows():
     res = run_lib_prefill(w, inp, cache=cache, rows=rows)
     for bi, row in ((0, 3), (1, 1)):
         for h in range(2):
-            _check_group(w, inp, res, bi, h, row=row)
+            check_prefill_group(w, inp, res, bi, h, row=row)
     assert (cache.slot_pos[0] == -1).all() and (cache.slot_pos[2] == -1).all()
 
 
 def test_prefill_llama8b_c4k_full_shape():
     # 16 requests x 8 kv-heads, 16384 -> 4096; every group against the oracle
-    _case(synth.workload("llama8b_c4k"), 11)
+    prefill_case(synth.workload("llama8b_c4k"), 11)
 
 
 def test_prefill_llama8b_128k_sampled_groups():
     # 8 requests x 8 kv-heads, 131072 -> 32768 on the GPU; the oracle checks
     # three (request, kv-head) groups one by one
-    _case(synth.workload("llama8b_128k"), 12, groups=[(0, 0), (3, 5), (7, 7)])
+    prefill_case(synth.workload("llama8b_128k"), 12, groups=[(0, 0), (3, 5), (7, 7)])
