@@ -116,7 +116,8 @@ def cpu_baseline(w, inp, dec, budget_s=12.0):
     t0 = time.perf_counter()
     n_req = 0
     results = []
-    while n_req < w["B"] and (time.perf_counter() - t0) < budget_s / 2:
+    n_avail = inp["k"].shape[0]
+    while n_req < n_avail and (time.perf_counter() - t0) < budget_s / 2:
         q = synth.to_f64(inp["q_obs"][n_req])
         k = synth.to_f64(inp["k"][n_req])
         v = synth.to_f64(inp["v"][n_req]) if inp["v"] is not None else None
