@@ -101,11 +101,10 @@ DecodePlan plan_decode(const ss_config* c, int B_max) {
   // balance rows of very different valid lengths).
   const long long tiles = (C + ss::DECODE_TILE - 1) / ss::DECODE_TILE;
   if (c->v_aliases_k) {
-    // latent (MLA) kernel: the 4 waves of a workgroup share each tile; aim
-    // for 512 workgroups (2 per CU) with at most 64 tiles each
-    long long want_wg = (512 + groups - 1) / groups;
+    // latent (MLA) kernel: the 4 waves of a workgroup share each tile
+    long long want_wg = (ss::MLA_TARGET_WG + groups - 1) / groups;
     long long tpg = (tiles + want_wg - 1) / want_wg;
-    if (tpg > 64) tpg = 64;
+    if (tpg > ss::MLA_MAX_TILES) tpg = ss::MLA_MAX_TILES;
     if (tpg < 1) tpg = 1;
     p.split = p.wsplit = static_cast<int>(tpg) * ss::DECODE_TILE;
   } else {

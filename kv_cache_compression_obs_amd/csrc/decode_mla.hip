@@ -38,9 +38,12 @@ constexpr int MNC = MD / 32;            // d-chunks of the Q.K^T contraction
 constexpr int MCW = cdiv(MNC, MW);      // at most this many chunks per wave
 constexpr int MNDB = MDV / 16 / MW;     // 16-wide value blocks per wave
 static_assert(MTS * MCH % MNT == 0, "tile split");
-static_assert(16 * MD * 4 <= MTS * MLROW, "query staging aliases the latent tile");
 
-__global__ __launch_bounds__(MNT) void decode_mla_kernel(DecodeArgs a) {
+#ifndef SS_MLA_WAVES_PER_EU
+#define SS_MLA_WAVES_PER_EU 2
+#endif
+__global__ __launch_bounds__(MNT) __attribute__((amdgpu_waves_per_eu(SS_MLA_WAVES_PER_EU))) void
+decode_mla_kernel(DecodeArgs a) {
   using MM = Mma<bf16_t>;
   using frag = MM::frag;
   __shared__ __attribute__((aligned(16))) char lat[MTS * MLROW];
@@ -86,37 +89,45 @@ __global__ __launch_bounds__(MNT) void decode_mla_kernel(DecodeArgs a) {
   };
 
   // ---------------------------------------------------------------- RoPE
-  // q / k_new elements and their rotation partners first, then the first tile
-  // (vector loads complete in issue order).
+  // Each lane loads the 8 query dims it feeds to the Q.K^T contraction (head
+  // col, dims c*32 + qg*8 .. +8 of this wave's chunks) and, inside the rotary
+  // range, the dims they pair with; the owner also loads the new latent row.
+  // Then the first tile is requested: vector loads complete in issue order,
+  // so the rotary work does not wait for the tile.
   const int half = a.rope_half;
   const bool rope = half > 0;
-  const int rb = a.rope_begin;
+  const int rb = a.rope_begin, re = rb + 2 * half;
   auto partner = [&](int d) __attribute__((always_inline)) {
-    if (!rope || d < rb || d >= rb + 2 * half) return d;
+    if (!rope || d < rb || d >= re) return d;
     return d - rb < half ? d + half : d - half;
   };
-  constexpr int QPT = cdiv(16 * MD, MNT), KPT = cdiv(MD, MNT);
-  bf16_t qx[QPT], qp[QPT], kx[KPT], kp[KPT];
-  {
-    const bf16_t* q = static_cast<const bf16_t*>(a.q) + head0 * MD;
+  const bool qlane = col < G;
+  const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + (head0 + (qlane ? col : 0)) * MD;
+  u32x4_t qv[MCW], qpv[MCW];
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int idx = tid + j * MNT;
-      if (idx < G * MD) {
-        const int d = idx % MD;
-        qx[j] = q[idx];
-        qp[j] = q[idx - d + partner(d)];
+  for (int j = 0; j < MCW; ++j) {
+    const int d0 = (clo + j) * 32 + qg * 8;
+    qv[j] = qpv[j] = u32x4_t{0u, 0u, 0u, 0u};
+    if (qlane && clo + j < chi) {
+      qv[j] = *reinterpret_cast<const u32x4_t*>(qrow + d0);
+      if (rope && d0 + 8 > rb && d0 < re) {
+        bf16_t e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = qrow[partner(d0 + e)];
+        qpv[j] = __builtin_bit_cast(u32x4_t, pack_bf16x8(e8));
       }
     }
-    if (own) {
-      const bf16_t* kn = static_cast<const bf16_t*>(a.k_new) + gh * MD;
+  }
+  constexpr int KPT = cdiv(MD, MNT);
+  bf16_t kx[KPT], kp[KPT];
+  if (own) {
+    const bf16_t* kn = static_cast<const bf16_t*>(a.k_new) + gh * MD;
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int d = tid + j * MNT;
-        if (d < MD) {
-          kx[j] = kn[d];
-          kp[j] = kn[partner(d)];
-        }
+    for (int j = 0; j < KPT; ++j) {
+      const int d = tid + j * MNT;
+      if (d < MD) {
+        kx[j] = kn[d];
+        kp[j] = kn[partner(d)];
       }
     }
   }
@@ -129,13 +140,6 @@ __global__ __launch_bounds__(MNT) void decode_mla_kernel(DecodeArgs a) {
     csn[half + i] = sv;
   }
   __syncthreads();
-  float* qs = reinterpret_cast<float*>(lat);  // [G, 576] rotated queries, fp32
-#pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const int idx = tid + j * MNT;
-    if (idx < G * MD)
-      qs[idx] = rotate_pair<bf16_t, float>(qx[j], qp[j], idx % MD, rope, rb, half, csn, csn + half);
-  }
   if (own) {
     bf16_t* kdst = static_cast<bf16_t*>(a.kc) + (gh * a.C + slot) * MD;
 #pragma unroll
@@ -155,17 +159,21 @@ __global__ __launch_bounds__(MNT) void decode_mla_kernel(DecodeArgs a) {
       }
     }
   }
-  __syncthreads();
-  // this wave's query chunks as B operands (hi + lo parts)
+  // this wave's rotated query chunks as B operands (hi + lo parts); lanes of
+  // heads >= G and chunks past the wave's range hold zeros
   frag qf[2][MCW];
 #pragma unroll
   for (int j = 0; j < MCW; ++j) {
-    const int c = clo + j;
-    float qv[8];
+    const int d0 = (clo + j) * 32 + qg * 8;
+    float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = (col < G && c < chi) ? qs[col * MD + c * 32 + qg * 8 + e] : 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const bf16_t x = static_cast<bf16_t>(qv[j][e >> 1] >> (16 * (e & 1)));
+      const bf16_t xp = static_cast<bf16_t>(qpv[j][e >> 1] >> (16 * (e & 1)));
+      v[e] = rotate_pair<bf16_t, float>(x, xp, d0 + e, rope, rb, half, csn, csn + half);
+    }
     frag parts[2];
-    Split<bf16_t>::make(qv, parts);
+    Split<bf16_t>::make(v, parts);
     qf[0][j] = parts[0];
     qf[1][j] = parts[1];
   }
@@ -178,7 +186,7 @@ __global__ __launch_bounds__(MNT) void decode_mla_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   for (int t0 = s0; t0 < s1; t0 += MTS) {
-    __syncthreads();  // the previous tile (or the queries) is no longer read
+    __syncthreads();  // the previous tile is no longer read; knew is visible
     // the new token: a tile row whose (clamped) slot is `slot` takes it from
     // LDS, never from the cache memory this launch just wrote; the thread that
     // stores a chunk also decides its source, so no two stores race

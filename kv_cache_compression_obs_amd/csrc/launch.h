@@ -76,6 +76,16 @@ constexpr int DECODE_WAVES = 4;   // waves per decode workgroup
 #ifndef SS_DECODE_MAX_TILES
 #define SS_DECODE_MAX_TILES 32
 #endif
+// Latent (MLA) decode grid: aim for this many workgroups when every slot is
+// valid, with at most SS_MLA_MAX_TILES tiles per workgroup.
+#ifndef SS_MLA_TARGET_WG
+#define SS_MLA_TARGET_WG 512
+#endif
+#ifndef SS_MLA_MAX_TILES
+#define SS_MLA_MAX_TILES 64
+#endif
+constexpr int MLA_TARGET_WG = SS_MLA_TARGET_WG;
+constexpr int MLA_MAX_TILES = SS_MLA_MAX_TILES;
 constexpr int DECODE_TARGET_WAVES = SS_DECODE_TARGET_WAVES;
 constexpr int DECODE_MAX_TILES = SS_DECODE_MAX_TILES;
 // LDS row stride of the decode V tile (bytes) for value rows of `row_bytes`
