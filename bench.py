@@ -14,7 +14,11 @@ own sequence position.
 
 Prints one JSON line.  `value` = algorithmic HBM bytes of the step (prefill:
 prompt keys read once + C cache rows gathered, read and written; decode: every
-valid cache row read) per second of wall time.
+valid cache row read) per second of wall time.  `roofline` prices the decode
+kernel: its average launch duration is the time between a HIP event recorded
+right before the step's first decode kernel and one right after its last,
+divided by the number of launches (so it includes the short gaps between
+back-to-back launches; no marker sits between them).
 """
 from __future__ import annotations
 
@@ -210,7 +214,7 @@ def main():
 
     hip = HipEvents()
     ev_score = [hip.create(2) for _ in range(total_steps)]
-    ev_attn = [hip.create(2 * n_dec) for _ in range(total_steps)]
+    ev_attn = [hip.create(2) for _ in range(total_steps)]
     tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total_steps)]
 
     def step(i):
@@ -224,8 +228,11 @@ def main():
         for t in range(n_dec):
             r = t % R
             vn = dec["v_new"][t] if dec["v_new"] is not None else None
+            # one event right before the first decode kernel and one right
+            # after the last: markers between launches would perturb them
+            evs = (ea[0] if t == 0 else None, ea[1] if t == n_dec - 1 else None)
             ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], vn, posbuf[count[r]], caches[r],
-                              out, err, ws_d, events=(ea[2 * t], ea[2 * t + 1]))
+                              out, err, ws_d, events=evs if any(evs) else None)
             count[r] += 1
         e[2].record()
 
@@ -244,8 +251,7 @@ def main():
     pre_ms = [tev[i][0].elapsed_time(tev[i][1]) for i in timed]
     dec_ms = [tev[i][1].elapsed_time(tev[i][2]) for i in timed]
     score_ms = [hip.elapsed_ms(ev_score[i][0], ev_score[i][1]) for i in timed]
-    attn_ms = [hip.elapsed_ms(ev_attn[i][2 * t], ev_attn[i][2 * t + 1])
-               for i in timed for t in range(n_dec)]
+    attn_ms = [hip.elapsed_ms(ev_attn[i][0], ev_attn[i][1]) / n_dec for i in timed]
     pre_b, dec_b = algorithmic_bytes(w, elem)
     step_b = pre_b + n_dec * dec_b
     attn_avg_s = sum(attn_ms) / len(attn_ms) / 1e3

@@ -60,7 +60,8 @@ typedef enum {
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
-/* One attention layer and its fixed cache.  C = L_sink + K + L_recent slots.
+/* One attention layer and its fixed cache.  C = L_sink + K + L_recent slots,
+ * at most 2^24 (larger C: SS_ERR_INVALID_ARG).
  * Supported (d_qk, d_v, dtype): (64, 64, f32|bf16), (128, 128, f32|bf16),
  * (576, 512, bf16) with v_aliases_k = 1 (MLA absorbed latent).  G = n_q_heads /
  * n_kv_heads must be an integer <= 16; G * W <= 256. */

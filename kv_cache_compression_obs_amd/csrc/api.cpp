@@ -34,8 +34,10 @@ ss_status check_config(const ss_config* c) {
         (c->rope_end - c->rope_begin) % 2 != 0)
       return SS_ERR_INVALID_ARG;
   }
+  // at most 2^24 slots: keeps every per-head partial range of the decode
+  // workspace addressable with 32-bit byte offsets
   const long long C = static_cast<long long>(c->L_sink) + c->K + c->L_recent;
-  if (C > (1LL << 30)) return SS_ERR_INVALID_ARG;
+  if (C > ss::MAX_CACHE_SLOTS) return SS_ERR_INVALID_ARG;
   if (c->dtype != SS_F32 && c->dtype != SS_BF16) return SS_ERR_INVALID_ARG;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (!supported_shape(c) || G > 16 || G * c->W > 256) return SS_ERR_UNSUPPORTED;

@@ -351,8 +351,6 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
                                        __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sh_ticket != ns - 1) return;
-  // Acquire once (drops this XCD's stale L2 lines), then ordinary loads.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   merge_splits<T, DV>(a, head0, G, ns, tid, 64 * DW);
   if (tid == 0) a.counter[gh] = 0;  // ready for the next call
 }

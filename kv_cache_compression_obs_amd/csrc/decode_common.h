@@ -27,6 +27,22 @@ __device__ __forceinline__ O rotate_pair(T x, T xp, int d, bool rope, int begin,
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Device-scope load (the access the compiler emits for an agent-scope relaxed
+// atomic load: it is served by the level shared by all XCDs, never by a stale
+// line of this XCD's L2).
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte device-scope loads: a raw buffer over [p, p + bytes) whose loads
+// carry the same device-scope (sc1) cache policy.
+constexpr int CPOL_SC1 = 16;
+constexpr int BUF_RSRC_WORD3 = 0x00020000;  // 32-bit data format, raw (stride 0) addressing
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_buffer(const float* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, bytes, BUF_RSRC_WORD3);
+}
+__device__ __forceinline__ f32x4_t ld_dev4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1));
+}
 __device__ __forceinline__ void st_dev4(float* p, f32x4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
@@ -91,7 +107,13 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // The last workgroup of a (row, kv-head) group merges every split's partial
-// (max m_s, sum l_s, unnormalised o_s, written with st_dev/st_dev4):
+// (max m_s, sum l_s, unnormalised o_s, written with st_dev/st_dev4).
+// Ordering: every writer waits for its partial stores to complete at the
+// device-coherent level before it takes its ticket; the merging workgroup
+// holds the last ticket, so all partials are there before it issues its
+// device-scope loads (ld_dev).  No acquire fence is needed: a fence would
+// invalidate this XCD's whole L2 and slow every workgroup still streaming on
+// it.  The merge computes
 //   out[head, dv] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
 // in split order.  Each thread loads every split's (m, l, o) of its 4
 // outputs at once (batches of MB splits): one memory round trip per batch.
@@ -102,6 +124,7 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, size_t head0, 
   for (int idx = tid; idx < G * (DV / 4); idx += nthreads) {
     const int g = idx / (DV / 4), d4 = idx % (DV / 4);
     const size_t base = (head0 + g) * a.n_split;
+    const __amdgpu_buffer_rsrc_t ob = dev_buffer(a.part_o + base * DV, a.n_split * DV * 4);
     float M = -INFINITY, L = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int sb = 0; sb < ns; sb += MB) {
@@ -111,10 +134,10 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, size_t head0, 
       for (int j = 0; j < MB; ++j) {
         const bool in = sb + j < ns;
         const size_t s = base + sb + (in ? j : 0);
-        mv[j] = in ? a.part_ml[2 * s] : -INFINITY;
-        lv[j] = in ? a.part_ml[2 * s + 1] : 0.f;
-        ov[j] = in ? *reinterpret_cast<const f32x4_t*>(a.part_o + s * DV + 4 * d4)
-                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        mv[j] = in ? ld_dev(a.part_ml + 2 * s) : -INFINITY;
+        lv[j] = in ? ld_dev(a.part_ml + 2 * s + 1) : 0.f;
+        ov[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (in) ov[j] = ld_dev4(ob, ((sb + j) * DV + 4 * d4) * 4);
       }
       float Mn = M;
 #pragma unroll

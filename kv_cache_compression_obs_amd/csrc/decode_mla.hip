@@ -276,7 +276,6 @@ decode_mla_kernel(DecodeArgs a) {
                                        __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sh_ticket != ns - 1) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   merge_splits<bf16_t, MDV>(a, head0, G, ns, tid, MNT);
   if (tid == 0) a.counter[gh] = 0;  // ready for the next call
 }

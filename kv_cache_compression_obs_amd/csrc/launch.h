@@ -7,6 +7,7 @@
 namespace ss {
 
 constexpr int ROPE_MAX_PAIRS = 64;  // rotary range of at most 128 dims
+constexpr long long MAX_CACHE_SLOTS = 1LL << 24;
 
 struct DecodeArgs {
   const void* q;         // [B, Hq, D] pre-RoPE

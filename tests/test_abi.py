@@ -56,6 +56,7 @@ def test_cache_slots_and_workspace_sizes():
     (dict(rope_end=129), ss.SS_ERR_INVALID_ARG),
     (dict(rope_begin=1), ss.SS_ERR_INVALID_ARG),
     (dict(dtype=7), ss.SS_ERR_INVALID_ARG),
+    (dict(L_recent=(1 << 24)), ss.SS_ERR_INVALID_ARG),   # more than 2^24 cache slots
     (dict(d_qk=96, d_v=96, rope_end=96), ss.SS_ERR_UNSUPPORTED),
     (dict(n_q_heads=8 * 17), ss.SS_ERR_UNSUPPORTED),
 ])
