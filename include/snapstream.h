@@ -1,7 +1,9 @@
 /*
  * libsnapstream: the data-parallel hot path of SnapStream (fixed-size KV cache
  * built at prefill, ring-buffer decode over it) for AMD Instinct MI355X
- * (gfx950).  Plain C ABI; every buffer is caller-owned.
+ * (gfx950).  Plain C ABI; every buffer is caller-owned.  Tensor and workspace
+ * pointers are device addresses aligned to 16 bytes (SS_ERR_INVALID_ARG
+ * otherwise): the kernels move data in 16-byte vectors.
  *
  * Sources, by page title and section:
  *   "SnapStream: Efficient Long Sequence Decoding on Dataflow Accelerators",
@@ -63,7 +65,8 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 /* One attention layer and its fixed cache.  C = L_sink + K + L_recent slots,
  * at most 2^24 (larger C: SS_ERR_INVALID_ARG).
  * Supported (d_qk, d_v, dtype): (64, 64, f32|bf16), (128, 128, f32|bf16),
- * (576, 512, bf16) with v_aliases_k = 1 (MLA absorbed latent).  G = n_q_heads /
+ * (576, 512, bf16) with v_aliases_k = 1 (MLA absorbed latent; its rotary range,
+ * if any, must start on a multiple of 8 dims and span a multiple of 16).  G = n_q_heads /
  * n_kv_heads must be an integer <= 16; G * W <= 256. */
 typedef struct {
   int32_t n_q_heads;

@@ -1,6 +1,7 @@
 // C ABI of libsnapstream: argument checks, workspace carving and kernel
 // launches.  No allocation, no host synchronisation, no global state.
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "snapstream.h"
@@ -12,8 +13,11 @@ constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool supported_shape(const ss_config* c) {
-  if (c->v_aliases_k)  // MLA absorbed latent: 512 value dims + 64 rotary dims, bf16
-    return c->dtype == SS_BF16 && c->d_qk == 576 && c->d_v == 512;
+  if (c->v_aliases_k)  // MLA absorbed latent: 512 value dims + rotary dims, bf16; the
+                       // rotary range starts and splits on multiples of 8 dims
+    return c->dtype == SS_BF16 && c->d_qk == 576 && c->d_v == 512 &&
+           (c->rope_theta == 0.f ||
+            (c->rope_begin % 8 == 0 && (c->rope_end - c->rope_begin) % 16 == 0));
   if (c->dtype != SS_F32 && c->dtype != SS_BF16) return false;
   return (c->d_qk == 64 && c->d_v == 64) || (c->d_qk == 128 && c->d_v == 128);
 }
@@ -45,6 +49,9 @@ ss_status check_config(const ss_config* c) {
     return SS_ERR_UNSUPPORTED;
   return SS_OK;
 }
+
+// Tensors are read and written in 16-byte vectors.
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
 
 int cache_slots(const ss_config* c) { return c->L_sink + c->K + c->L_recent; }
 float scale_log2(const ss_config* c) {
@@ -180,6 +187,9 @@ ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, c
       cache->slot_pos == nullptr || cache->n_tokens == nullptr || cache->B_max < 1)
     return SS_ERR_INVALID_ARG;
   if (!cfg->v_aliases_k && (v == nullptr || cache->v == nullptr)) return SS_ERR_INVALID_ARG;
+  if (misaligned(q_obs) || misaligned(k) || misaligned(v) || misaligned(cache->k) ||
+      misaligned(cache->v) || misaligned(ws))
+    return SS_ERR_INVALID_ARG;
   if (rows == nullptr && b > cache->B_max) return SS_ERR_INVALID_ARG;
   const int C = cache_slots(cfg);
   const bool compressed = L > C;
@@ -249,6 +259,9 @@ ss_status decode_impl(const ss_config* cfg, const void* q, const void* k_new, co
       cache->B_max < 1)
     return SS_ERR_INVALID_ARG;
   if (!cfg->v_aliases_k && (v_new == nullptr || cache->v == nullptr)) return SS_ERR_INVALID_ARG;
+  if (misaligned(q) || misaligned(k_new) || misaligned(v_new) || misaligned(cache->k) ||
+      misaligned(cache->v) || misaligned(ws))
+    return SS_ERR_INVALID_ARG;
   const DecodePlan p = plan_decode(cfg, cache->B_max);
   if (ws == nullptr || ws_bytes < p.total) return SS_ERR_WORKSPACE;
 

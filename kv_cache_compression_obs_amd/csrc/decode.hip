@@ -57,7 +57,10 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   constexpr int NP = Split<T>::N;
   constexpr int WBYTES = TS * LROW;  // one wave's V tile
   static_assert(D % KSTEP == 0 && DV % 64 == 0 && (TS * VCH) % 64 == 0, "tile shape");
-  static_assert(DW * WBYTES >= 16 * D * 4, "query staging must fit in the V tiles");
+  static_assert(DW * WBYTES >= 16 * D * 4 + 17 * D * static_cast<int>(sizeof(T)),
+                "query staging must fit in the V tiles");
+  static_assert(VROW <= 64 * DW * 16 && D * static_cast<int>(sizeof(T)) <= 64 * DW * 16,
+                "one 16-byte load per thread covers a k / v row");
   static_assert(WBYTES >= 16 * DV * 4, "a wave's partial must fit in its V tile");
   __shared__ __attribute__((aligned(16))) char vt_all[DW * WBYTES];
   __shared__ double csn[D];
@@ -69,9 +72,65 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
-  const int p = a.pos[b];
+  // pos as a vector load: waiting for it does not wait for the loads after it
+  const int pv = __hip_atomic_load(a.pos + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const size_t gh = static_cast<size_t>(b) * a.Hkv + h;
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(h) * G;
+  const int col = lane & 15, qg = lane >> 4;
+  const T* kb = static_cast<const T*>(a.kc) + gh * a.C * D;
+  const T* vb = ALIAS ? kb : static_cast<const T*>(a.vc) + gh * a.C * DV;
+  const int koff = 4 * (col & 3) + (col >> 2);
+  frag kf[2][NC];
+  u32x4_t vr[VLD];
+  // Tile [t0, t0 + 32) into registers; rows at or past `hi` read row hi - 1.
+  // Always inlined: the register arrays it fills must not become stack memory.
+  auto load_tile = [&](int t0, int hi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int s = min(t0 + 16 * h2 + koff, hi - 1);
+      const T* kr = kb + static_cast<size_t>(s) * D + qg * KPL;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kf[h2][c] = MM::load(kr + c * KSTEP);
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int id = i * 64 + lane;
+      const int s = min(t0 + id / VCH, hi - 1);
+      vr[i] = *reinterpret_cast<const u32x4_t*>(
+          reinterpret_cast<const char*>(vb + static_cast<size_t>(s) * VSTRIDE) + (id % VCH) * 16);
+    }
+  };
+  // ---------------------------------------------------------------- loads
+  // In this order (vector loads complete in issue order): pos, the G queries
+  // and the new token's k / v rows as 16-byte vectors, then (once pos has
+  // given this wave's slots) the first tile, whose latency covers the rotary
+  // work.  If the tile holds the new token's slot, the stale row it reads is
+  // replaced from LDS in the main loop.
+  const int half = a.rope_half;
+  const bool rope = half > 0;
+  const int rb = a.rope_begin;
+  auto partner = [&](int d) __attribute__((always_inline)) {
+    if (!rope || d < rb || d >= rb + 2 * half) return d;
+    return d - rb < half ? d + half : d - half;
+  };
+  constexpr int NT = 64 * DW;
+  constexpr int KROW = D * static_cast<int>(sizeof(T));   // bytes of one q / k row
+  constexpr int QLD = cdiv(16 * KROW, NT * 16);           // 16-byte query loads per thread
+  const int qbytes = G * KROW;
+  const char* qsrc = reinterpret_cast<const char*>(static_cast<const T*>(a.q) + head0 * D);
+  const char* ksrc = reinterpret_cast<const char*>(static_cast<const T*>(a.k_new) + gh * D);
+  u32x4_t qld[QLD], kld, vld;
+#pragma unroll
+  for (int j = 0; j < QLD; ++j) {
+    const int off = (tid + j * NT) * 16;
+    if (off < qbytes) qld[j] = *reinterpret_cast<const u32x4_t*>(qsrc + off);
+  }
+  if (tid * 16 < KROW) kld = *reinterpret_cast<const u32x4_t*>(ksrc + tid * 16);
+  if (!ALIAS && tid * 16 < VROW)
+    vld = *reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const char*>(static_cast<const T*>(a.v_new) + gh * DV) + tid * 16);
+
+  const int p = __builtin_amdgcn_readfirstlane(pv);
   if (p < 0) {  // inactive row: output 0, no state change
     if (split == 0) {
       T* o = static_cast<T*>(a.out) + head0 * DV;
@@ -86,80 +145,23 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   const int s1 = min(s0 + a.split, n_valid);
   const int w0 = min(s0 + wave * a.wsplit, s1);  // this wave's slots [w0, w1)
   const int w1 = min(w0 + a.wsplit, s1);
+  if (w0 < w1) load_tile(w0, w1);  // the first tile, in flight during the rotary work
   const int SK = a.S + a.K;
   const int slot = p < SK ? p : SK + (p - SK) % a.R;
   const bool own = slot >= s0 && slot < s1;
   const bool wown = slot >= w0 && slot < w1;
-  const int col = lane & 15, qg = lane >> 4;
-
-  const T* kb = static_cast<const T*>(a.kc) + gh * a.C * D;
-  const T* vb = ALIAS ? kb : static_cast<const T*>(a.vc) + gh * a.C * DV;
-  const int koff = 4 * (col & 3) + (col >> 2);
-  frag kf[2][NC];
-  u32x4_t vr[VLD];
-  // always inlined: the register arrays it fills must not become stack memory
-  auto load_tile = [&](int t0) __attribute__((always_inline)) {
+  // raw query / k_new rows into LDS behind the rotated-query area (all of it
+  // is V tile space again once the main loop starts); v_new straight to vnew
+  float* qs = reinterpret_cast<float*>(vt_all);                  // [G, D] rotated, fp32
+  T* qraw = reinterpret_cast<T*>(vt_all + 16 * D * 4);          // [G, D] as given
+  T* kraw = qraw + 16 * D;                                       // [D] as given
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int s = min(t0 + 16 * h2 + koff, w1 - 1);
-      const T* kr = kb + static_cast<size_t>(s) * D + qg * KPL;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kf[h2][c] = MM::load(kr + c * KSTEP);
-    }
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int id = i * 64 + lane;
-      const int s = min(t0 + id / VCH, w1 - 1);
-      vr[i] = *reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const char*>(vb + static_cast<size_t>(s) * VSTRIDE) + (id % VCH) * 16);
-    }
-  };
-  // ---------------------------------------------------------------- RoPE
-  // The new token's q / k_new / v_new elements (and their rotation partners)
-  // are loaded first, then the first tile is requested: vector loads complete
-  // in issue order, so the rotary work does not wait for the tile, while the
-  // tile's latency covers the rotary work.  If the tile holds the new token's
-  // slot, the stale row it reads is replaced from LDS in the main loop.
-  const int half = a.rope_half;
-  const bool rope = half > 0;
-  const int rb = a.rope_begin;
-  auto partner = [&](int d) __attribute__((always_inline)) {
-    if (!rope || d < rb || d >= rb + 2 * half) return d;
-    return d - rb < half ? d + half : d - half;
-  };
-  constexpr int NT = 64 * DW;
-  constexpr int QPT = cdiv(16 * D, NT), KPT = cdiv(D, NT), VPT = cdiv(DV, NT);
-  T qx[QPT], qp[QPT], kx[KPT], kp[KPT], vx[VPT];
-  {
-    const T* q = static_cast<const T*>(a.q) + head0 * D;
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int idx = tid + j * NT;
-      if (idx < G * D) {
-        const int d = idx % D;
-        qx[j] = q[idx];
-        qp[j] = q[idx - d + partner(d)];
-      }
-    }
-    if (own) {
-      const T* kn = static_cast<const T*>(a.k_new) + gh * D;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int d = tid + j * NT;
-        if (d < D) {
-          kx[j] = kn[d];
-          kp[j] = kn[partner(d)];
-        }
-      }
-      if (!ALIAS) {
-        const T* vn = static_cast<const T*>(a.v_new) + gh * DV;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j)
-          if (tid + j * NT < DV) vx[j] = vn[tid + j * NT];
-      }
-    }
+  for (int j = 0; j < QLD; ++j) {
+    const int off = (tid + j * NT) * 16;
+    if (off < qbytes) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(qraw) + off) = qld[j];
   }
-  if (w0 < w1) load_tile(w0);
+  if (tid * 16 < KROW) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(kraw) + tid * 16) = kld;
+  if (!ALIAS && tid * 16 < VROW) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(vnew) + tid * 16) = vld;
   for (int i = tid; i < half; i += NT) {
     const double ang = static_cast<double>(p) * a.inv_freq[i];
     double sv, cv;
@@ -168,35 +170,21 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
     csn[half + i] = sv;
   }
   __syncthreads();
-  float* qs = reinterpret_cast<float*>(vt_all);  // [G, D] rotated queries, fp32
-#pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const int idx = tid + j * NT;
-    if (idx < G * D)
-      qs[idx] = rotate_pair<T, float>(qx[j], qp[j], idx % D, rope, rb, half, csn, csn + half);
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int d = idx % D;
+    qs[idx] = rotate_pair<T, float>(qraw[idx], qraw[idx - d + partner(d)], d, rope, rb, half, csn,
+                                    csn + half);
   }
   if (own) {
     T* kdst = static_cast<T*>(a.kc) + (gh * a.C + slot) * D;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int d = tid + j * NT;
-      if (d < D) {
-        const T kv = rotate_pair<T, T>(kx[j], kp[j], d, rope, rb, half, csn, csn + half);
-        knew[d] = kv;
-        kdst[d] = kv;
-      }
+    for (int d = tid; d < D; d += NT) {
+      const T kv = rotate_pair<T, T>(kraw[d], kraw[partner(d)], d, rope, rb, half, csn, csn + half);
+      knew[d] = kv;
+      kdst[d] = kv;
     }
-    if (!ALIAS) {
-      T* vdst = static_cast<T*>(a.vc) + (gh * a.C + slot) * DV;
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        const int d = tid + j * NT;
-        if (d < DV) {
-          vnew[d] = vx[j];
-          vdst[d] = vx[j];
-        }
-      }
-    }
+    if (!ALIAS && tid * 16 < VROW)
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(static_cast<T*>(a.vc) +
+                                                          (gh * a.C + slot) * DV) + tid * 16) = vld;
     if (tid == 0) {
       a.slot_pos[gh * a.C + slot] = p;
       if (h == 0) {
@@ -254,7 +242,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
           for (int i = lane; i < VROW / 4; i += 64)
             reinterpret_cast<uint32_t*>(vt + r * LROW)[i] = reinterpret_cast<const uint32_t*>(vnew)[i];
     }
-    if (t0 + TS < w1) load_tile(t0 + TS);  // next tile in flight during this one
+    if (t0 + TS < w1) load_tile(t0 + TS, w1);  // next tile in flight during this one
 
     f32x4_t sacc[2];
 #pragma unroll

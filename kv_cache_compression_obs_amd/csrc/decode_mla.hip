@@ -50,14 +50,70 @@ decode_mla_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) f32x4_t sx[MW][2][64];
   __shared__ double csn[2 * ROPE_MAX_PAIRS];
   __shared__ __attribute__((aligned(16))) bf16_t knew[MD];
+  __shared__ __attribute__((aligned(16))) bf16_t kraw[MD];
   __shared__ int sh_ticket;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
-  const int p = a.pos[b];
+  // pos as a vector load: waiting for it does not wait for the loads after it
+  const int pv = __hip_atomic_load(a.pos + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const size_t gh = static_cast<size_t>(b) * a.Hkv + h;
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(h) * G;
+  const int col = lane & 15, qg = lane >> 4;
+  const int clo = MNC * wave / MW, chi = MNC * (wave + 1) / MW;  // this wave's d-chunks
+  const int s0 = split * a.split;
+
+  const bf16_t* lb = static_cast<const bf16_t*>(a.kc) + gh * a.C * MD;
+  u32x4_t pre[MLD];
+  // tile [t0, t0 + 32) into registers; rows at or past `hi` read row hi - 1
+  auto load_tile = [&](int t0, int hi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MLD; ++i) {
+      const int id = i * MNT + tid;
+      const int s = min(t0 + id / MCH, hi - 1);
+      pre[i] = *reinterpret_cast<const u32x4_t*>(
+          reinterpret_cast<const char*>(lb + static_cast<size_t>(s) * MD) + (id % MCH) * 16);
+    }
+  };
+
+  // ---------------------------------------------------------------- loads
+  // In this order (vector loads complete in issue order): pos; each lane's 8
+  // query dims of the Q.K^T contraction (head col, dims c*32 + qg*8 .. +8 of
+  // this wave's chunks) and, inside the rotary range, the dims they pair
+  // with; the new latent row; then (once pos has given the split's valid
+  // end) the first tile, whose latency covers the rotary work.
+  const int half = a.rope_half;
+  const bool rope = half > 0;
+  const int rb = a.rope_begin, re = rb + 2 * half;
+  auto partner = [&](int d) __attribute__((always_inline)) {
+    if (!rope || d < rb || d >= re) return d;
+    return d - rb < half ? d + half : d - half;
+  };
+  const bool qlane = col < G;
+  const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + (head0 + (qlane ? col : 0)) * MD;
+  // Unconditional loads (a lane past the wave's chunks rereads its last one;
+  // lanes of heads >= G read head 0): no branch, so no wait is forced here.
+  // The rotary range starts and splits on multiples of 8 dims (checked on the
+  // host), so the 8 partners of 8 aligned dims are 8 aligned consecutive dims.
+  // Outside the range the partner value is not used; the load then reads the
+  // neighbouring 8 dims (d0 ^ 8, same row), an address the compiler cannot
+  // fold into the query load.
+  u32x4_t qv[MCW], qpv[MCW];
+#pragma unroll
+  for (int j = 0; j < MCW; ++j) {
+    const int d0 = min(clo + j, chi - 1) * 32 + qg * 8;
+    const bool inr = rope && d0 >= rb && d0 < re;
+    const int pd = inr ? (d0 - rb < half ? d0 + half : d0 - half) : (d0 ^ 8);
+    qv[j] = *reinterpret_cast<const u32x4_t*>(qrow + d0);
+    qpv[j] = *reinterpret_cast<const u32x4_t*>(qrow + pd);
+  }
+  // the new latent row as given, 16 bytes per thread (threads past the row
+  // reread its last chunk)
+  const u32x4_t kld = *reinterpret_cast<const u32x4_t*>(static_cast<const bf16_t*>(a.k_new) +
+                                                         gh * MD + 8 * min(tid, MCH - 1));
+
+  const int p = __builtin_amdgcn_readfirstlane(pv);
   if (p < 0) {  // inactive row: output 0, no state change
     if (split == 0) {
       bf16_t* o = static_cast<bf16_t*>(a.out) + head0 * MDV;
@@ -68,70 +124,12 @@ decode_mla_kernel(DecodeArgs a) {
   const int n_valid = min(p + 1, a.C);
   const int ns = cdiv(n_valid, a.split);
   if (split >= ns) return;
-  const int s0 = split * a.split;
   const int s1 = min(s0 + a.split, n_valid);
+  load_tile(s0, s1);  // the first tile, in flight during the rotary work
   const int SK = a.S + a.K;
   const int slot = p < SK ? p : SK + (p - SK) % a.R;
   const bool own = slot >= s0 && slot < s1;
-  const int col = lane & 15, qg = lane >> 4;
-  const int clo = MNC * wave / MW, chi = MNC * (wave + 1) / MW;  // this wave's d-chunks
-
-  const bf16_t* lb = static_cast<const bf16_t*>(a.kc) + gh * a.C * MD;
-  u32x4_t pre[MLD];
-  auto load_tile = [&](int t0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < MLD; ++i) {
-      const int id = i * MNT + tid;
-      const int s = min(t0 + id / MCH, s1 - 1);
-      pre[i] = *reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const char*>(lb + static_cast<size_t>(s) * MD) + (id % MCH) * 16);
-    }
-  };
-
-  // ---------------------------------------------------------------- RoPE
-  // Each lane loads the 8 query dims it feeds to the Q.K^T contraction (head
-  // col, dims c*32 + qg*8 .. +8 of this wave's chunks) and, inside the rotary
-  // range, the dims they pair with; the owner also loads the new latent row.
-  // Then the first tile is requested: vector loads complete in issue order,
-  // so the rotary work does not wait for the tile.
-  const int half = a.rope_half;
-  const bool rope = half > 0;
-  const int rb = a.rope_begin, re = rb + 2 * half;
-  auto partner = [&](int d) __attribute__((always_inline)) {
-    if (!rope || d < rb || d >= re) return d;
-    return d - rb < half ? d + half : d - half;
-  };
-  const bool qlane = col < G;
-  const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + (head0 + (qlane ? col : 0)) * MD;
-  u32x4_t qv[MCW], qpv[MCW];
-#pragma unroll
-  for (int j = 0; j < MCW; ++j) {
-    const int d0 = (clo + j) * 32 + qg * 8;
-    qv[j] = qpv[j] = u32x4_t{0u, 0u, 0u, 0u};
-    if (qlane && clo + j < chi) {
-      qv[j] = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-      if (rope && d0 + 8 > rb && d0 < re) {
-        bf16_t e8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) e8[e] = qrow[partner(d0 + e)];
-        qpv[j] = __builtin_bit_cast(u32x4_t, pack_bf16x8(e8));
-      }
-    }
-  }
-  constexpr int KPT = cdiv(MD, MNT);
-  bf16_t kx[KPT], kp[KPT];
-  if (own) {
-    const bf16_t* kn = static_cast<const bf16_t*>(a.k_new) + gh * MD;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int d = tid + j * MNT;
-      if (d < MD) {
-        kx[j] = kn[d];
-        kp[j] = kn[partner(d)];
-      }
-    }
-  }
-  load_tile(s0);
+  if (tid < MCH) reinterpret_cast<u32x4_t*>(kraw)[tid] = kld;
   for (int i = tid; i < half; i += MNT) {
     const double ang = static_cast<double>(p) * a.inv_freq[i];
     double sv, cv;
@@ -142,14 +140,11 @@ decode_mla_kernel(DecodeArgs a) {
   __syncthreads();
   if (own) {
     bf16_t* kdst = static_cast<bf16_t*>(a.kc) + (gh * a.C + slot) * MD;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int d = tid + j * MNT;
-      if (d < MD) {
-        const bf16_t kv = rotate_pair<bf16_t, bf16_t>(kx[j], kp[j], d, rope, rb, half, csn, csn + half);
-        knew[d] = kv;
-        kdst[d] = kv;
-      }
+    for (int d = tid; d < MD; d += MNT) {
+      const bf16_t kv = rotate_pair<bf16_t, bf16_t>(kraw[d], kraw[partner(d)], d, rope, rb, half,
+                                                    csn, csn + half);
+      knew[d] = kv;
+      kdst[d] = kv;
     }
     if (tid == 0) {
       a.slot_pos[gh * a.C + slot] = p;
@@ -165,12 +160,13 @@ decode_mla_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < MCW; ++j) {
     const int d0 = (clo + j) * 32 + qg * 8;
+    const bool live = qlane && clo + j < chi;
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const bf16_t x = static_cast<bf16_t>(qv[j][e >> 1] >> (16 * (e & 1)));
       const bf16_t xp = static_cast<bf16_t>(qpv[j][e >> 1] >> (16 * (e & 1)));
-      v[e] = rotate_pair<bf16_t, float>(x, xp, d0 + e, rope, rb, half, csn, csn + half);
+      v[e] = live ? rotate_pair<bf16_t, float>(x, xp, d0 + e, rope, rb, half, csn, csn + half) : 0.f;
     }
     frag parts[2];
     Split<bf16_t>::make(v, parts);
@@ -200,7 +196,7 @@ decode_mla_kernel(DecodeArgs a) {
       *reinterpret_cast<u32x4_t*>(lat + r * MLROW + c * 16) = v;
     }
     __syncthreads();  // tile visible
-    if (t0 + MTS < s1) load_tile(t0 + MTS);  // next tile in flight during this one
+    if (t0 + MTS < s1) load_tile(t0 + MTS, s1);  // next tile in flight during this one
 
     f32x4_t sacc[2];
 #pragma unroll

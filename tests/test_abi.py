@@ -96,6 +96,7 @@ def test_mla_latent_config_is_accepted():
     (dict(d_v=640), ss.SS_ERR_INVALID_ARG),              # value longer than the latent
     (dict(v_aliases_k=False), ss.SS_ERR_UNSUPPORTED),    # a separate 512-dim value cache
     (dict(n_q_heads=32), ss.SS_ERR_UNSUPPORTED),         # G * W = 1024 score rows
+    (dict(rope_begin=508), ss.SS_ERR_UNSUPPORTED),       # rotary range off the 8-dim grid
 ])
 def test_mla_unsupported_shapes_are_rejected(bad, code):
     cfg = _mla(**bad)
@@ -132,6 +133,13 @@ def test_null_pointers_and_small_workspace_are_rejected():
     assert lib.ss_prefill_compress(ctypes.byref(bad), fake, fake, fake, 2, 16384, None,
                                    ctypes.byref(cache), None, None, None, fake, 1 << 40,
                                    None) in (ss.SS_ERR_INVALID_ARG, ss.SS_ERR_UNSUPPORTED)
+    # a tensor pointer off the 16-byte grid
+    odd = ctypes.c_void_p(0x1008)
+    assert lib.ss_decode_step(ctypes.byref(cfg), odd, fake, fake, fake, ctypes.byref(cache), fake,
+                              None, fake, 1 << 30, None) == ss.SS_ERR_INVALID_ARG
+    assert lib.ss_prefill_compress(ctypes.byref(cfg), fake, odd, fake, 2, 16384, None,
+                                   ctypes.byref(cache), None, None, None, fake, 1 << 40,
+                                   None) == ss.SS_ERR_INVALID_ARG
     # more requests than cache rows without an explicit row map
     assert lib.ss_prefill_compress(ctypes.byref(cfg), fake, fake, fake, 17, 100, None,
                                    ctypes.byref(cache), None, None, None, fake, 1 << 30,
