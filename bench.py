@@ -155,6 +155,49 @@ def cpu_baseline(w, inp, dec, budget_s=12.0):
     }
 
 
+def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_s):
+    """The same decode over a cache that keeps the whole prompt (C = L: the
+    recent window widened to L - L_sink - K, so the prompt is stored as it is
+    and every slot is valid), timed like the compressed decode: what the
+    fixed-size cache saves per decode step."""
+    B, L = w["B"], w["L"]
+    wu = dict(w, L_recent=L - w["L_sink"] - w["K"])
+    wu["C"] = L
+    cfg_u = ss.make_config(**wu)
+    caches = [ss.Cache(cfg_u, B) for _ in range(R)]
+    for c in caches:
+        ss.ss_prefill_compress(cfg_u, inp["q_obs"], inp["k"], inp["v"], c)
+    ws = ss.decode_workspace(cfg_u, B)
+    dt = ss.TORCH_DTYPE[cfg.dtype]
+    out = torch.empty(B, w["n_q_heads"], w["d_v"], dtype=dt, device="cuda")
+    n = min(n_dec, 64)
+    pos = (L + torch.arange(n, dtype=torch.int32, device="cuda") // R)[:, None].repeat(1, B)
+    ev = hip.create(2)
+    for t in range(n):                     # warm-up pass at positions L.., then the timed pass
+        vn = dec["v_new"][t] if dec["v_new"] is not None else None
+        ss.ss_decode_step(cfg_u, dec["q"][t], dec["k_new"][t], vn, pos[t], caches[t % R], out,
+                          ws=ws)
+    pos += (n + R - 1) // R
+    for t in range(n):
+        vn = dec["v_new"][t] if dec["v_new"] is not None else None
+        evs = (ev[0] if t == 0 else None, ev[1] if t == n - 1 else None)
+        ss.ss_decode_step(cfg_u, dec["q"][t], dec["k_new"][t], vn, pos[t], caches[t % R], out,
+                          ws=ws, events=evs if any(evs) else None)
+    torch.cuda.synchronize()
+    step_s = hip.elapsed_ms(ev[0], ev[1]) / n / 1e3
+    hip.destroy(ev)
+    elem = 2 if w["dtype"] == "bf16" else 4
+    _, dec_b = algorithmic_bytes(wu, elem)
+    return {
+        "cache_slots": L,
+        "decode_step_us": round(1e6 * step_s, 2),
+        "decode_attn_GBps": round(dec_b / step_s / 1e9, 1),
+        "kv_bytes_ratio": round(L / w["C"], 3),
+        "decode_speedup_of_fixed_cache": round(step_s / attn_s, 3),
+        "note": f"{n} decode launches over a cache holding all {L} prompt tokens",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -165,6 +208,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-uncompressed", action="store_true",
+                    help="skip the uncompressed-cache baseline (decode over C = L slots)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (a kernel of "
                          "known traffic, to calibrate FETCH_SIZE/WRITE_SIZE counters)")
@@ -302,6 +347,10 @@ def main():
             "frac_bf16_peak_executed": round(fl_exec / score_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         },
     }
+    if not args.no_uncompressed:
+        caches.clear()                      # frees the compressed copies
+        res["uncompressed_baseline"] = uncompressed_baseline(
+            ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_avg_s)
     hip.destroy([e for p in ev_score for e in p] + [e for p in ev_attn for e in p])
     if not args.no_cpu_baseline:
         cpu_inp = {k: (v[:16] if v is not None else None) for k, v in inp.items()}

@@ -87,6 +87,16 @@ def test_decode_llama8b_c4k_full_shape():
     say(f"  worst max-abs {worst:.3g}")
 
 
+def test_decode_uncompressed_128k_cache():
+    # the uncompressed baseline's shape: a cache of C = L = 131072 slots that
+    # holds the whole prompt as it is (no scoring), every slot valid; the
+    # decode steps evict from the start of the recent window
+    w = synth.workload("llama8b_128k", B=2, L_recent=131072 - 64 - 960)
+    say("decode uncompressed C=L=131072 B=2 steps=2")
+    worst = decode_case(w, L=131072, steps=2, seed=10)
+    say(f"  worst max-abs {worst:.3g}")
+
+
 def test_decode_is_deterministic_and_workspace_reusable():
     # same inputs on two copies of the cache give bitwise-identical outputs
     # (fixed split order), and a workspace reused for many calls stays valid
