@@ -155,6 +155,39 @@ def cpu_baseline(w, inp, dec, budget_s=12.0):
     }
 
 
+def given_lse_prefill(ss, torch, w, cfg, inp, reps=5):
+    """ss_prefill_compress_lse (one score pass) on the same batch.  The
+    observation rows' log-sum-exp, which a prefill attention hands over, is
+    prepared beforehand with torch (fp32) and is not timed."""
+    import math
+    q, k = inp["q_obs"], inp["k"]
+    b, Hq, W, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    scale = w.get("scale", 0.0) or 1.0 / math.sqrt(d)
+    vis = torch.arange(L, device="cuda")[None, :] <= (L - W + torch.arange(W, device="cuda"))[:, None]
+    lse = torch.empty(b, Hq, W, dtype=torch.float32, device="cuda")
+    for bi in range(b):
+        for h in range(Hkv):
+            kt = k[bi, h].float().t().contiguous()
+            z = scale * (q[bi, h * G:(h + 1) * G].float().reshape(G * W, d) @ kt)
+            z = z.view(G, W, L).masked_fill(~vis, -math.inf)
+            lse[bi, h * G:(h + 1) * G] = torch.logsumexp(z, dim=2)
+    cache = ss.Cache(cfg, b)
+    ws = torch.empty(ss.ss_prefill_workspace_bytes(cfg, b, L), dtype=torch.uint8, device="cuda")
+    ss.ss_prefill_compress(cfg, q, k, inp["v"], cache, ws=ws, lse=lse)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        ss.ss_prefill_compress(cfg, q, k, inp["v"], cache, ws=ws, lse=lse)
+    ev[1].record()
+    torch.cuda.synchronize()
+    return {"prefill_compress_ms_per_layer": round(ev[0].elapsed_time(ev[1]) / reps, 4),
+            "note": "ss_prefill_compress_lse: one score pass over the middle keys, the rows' "
+                    "log-sum-exp given"}
+
+
 def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_s):
     """The same decode over a cache that keeps the whole prompt (C = L: the
     recent window widened to L - L_sink - K, so the prompt is stored as it is
@@ -347,6 +380,7 @@ def main():
             "frac_bf16_peak_executed": round(fl_exec / score_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         },
     }
+    res["given_lse"] = given_lse_prefill(ss, torch, w, cfg, inp)
     if not args.no_uncompressed:
         caches.clear()                      # frees the compressed copies
         res["uncompressed_baseline"] = uncompressed_baseline(

@@ -145,6 +145,28 @@ ss_status ss_prefill_compress(const ss_config* cfg, const void* q_obs, const voi
                               int32_t* sel_out, void* ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* ss_prefill_compress for a caller that already holds the log-sum-exp of
+ * every observation row, as the prefill's own attention (a flash-attention
+ * forward) returns it.  The scoring then makes one pass over the middle keys
+ * instead of two (the row-statistics pass over all L keys is skipped); the
+ * result is the same reading of the score ("Two Ingredients, Fused": SnapKV's
+ * attention-based selection, here fed by the attention the prefill computed
+ * anyway).
+ *
+ *   lse_obs  device float [b, n_q_heads, W]: natural-log log-sum-exp of row r
+ *            of q-head j, log sum_{i <= L-W+r} exp(scale * q_obs[j, r] . k[i]),
+ *            with the config's softmax scale.  Required (NULL:
+ *            SS_ERR_INVALID_ARG) and read only when L > C.
+ *
+ * Every other argument, the workspace size and the results are those of
+ * ss_prefill_compress.  The scores follow the given lse: an lse off by d
+ * scales that row's probabilities by exp(-d). */
+ss_status ss_prefill_compress_lse(const ss_config* cfg, const void* q_obs, const void* k,
+                                  const void* v, int32_t b, int32_t L, const float* lse_obs,
+                                  const int32_t* rows, const ss_cache* cache, float* raw_out,
+                                  float* pooled_out, int32_t* sel_out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
 /* One decode step of every cache row ("Ring Buffer vs. Naive Slicing": write
  * the new key/value into its fixed ring slot, evicting position pos -
  * L_recent; then memory-bound attention over the fixed cache).
@@ -172,7 +194,8 @@ ss_status ss_decode_step(const ss_config* cfg, const void* q, const void* k_new,
 /* Profiling variants: identical to the calls above, and additionally record
  * `begin` / `end` on `stream` immediately before and after the dominant
  * kernels - the split-C attention kernel of ss_decode_step, the two score
- * passes (row statistics through column scores) of ss_prefill_compress.
+ * passes (row statistics through column scores) of ss_prefill_compress, the
+ * lse conversion and column-score pass of ss_prefill_compress_lse.
  * Either event may be NULL.  The events are caller-created (hipEventCreate);
  * the caller reads hipEventElapsedTime after its own synchronisation.  When a
  * prompt is stored uncompressed (L <= C) no score kernel runs and the two
@@ -182,6 +205,13 @@ ss_status ss_prefill_compress_timed(const ss_config* cfg, const void* q_obs, con
                                     const ss_cache* cache, float* raw_out, float* pooled_out,
                                     int32_t* sel_out, void* ws, size_t ws_bytes,
                                     hipStream_t stream, hipEvent_t begin, hipEvent_t end);
+ss_status ss_prefill_compress_lse_timed(const ss_config* cfg, const void* q_obs, const void* k,
+                                        const void* v, int32_t b, int32_t L,
+                                        const float* lse_obs, const int32_t* rows,
+                                        const ss_cache* cache, float* raw_out,
+                                        float* pooled_out, int32_t* sel_out, void* ws,
+                                        size_t ws_bytes, hipStream_t stream, hipEvent_t begin,
+                                        hipEvent_t end);
 ss_status ss_decode_step_timed(const ss_config* cfg, const void* q, const void* k_new,
                                const void* v_new, const int32_t* pos, const ss_cache* cache,
                                void* out, int32_t* err_flag, void* ws, size_t ws_bytes,

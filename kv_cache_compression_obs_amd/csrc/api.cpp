@@ -177,8 +177,11 @@ ss_status ss_decode_workspace_init(const ss_config* cfg, int32_t B_max, void* ws
 
 namespace {
 
+// lse_call: the ss_prefill_compress_lse entry points (the row log-sum-exp is
+// given; required when the prompt is compressed).
 ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, const void* v,
-                       int32_t b, int32_t L, const int32_t* rows, const ss_cache* cache,
+                       int32_t b, int32_t L, bool lse_call, const float* lse,
+                       const int32_t* rows, const ss_cache* cache,
                        float* raw_out, float* pooled_out, int32_t* sel_out, void* ws,
                        size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const ss_status cs = check_config(cfg);
@@ -196,6 +199,8 @@ ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, c
   if (compressed) {
     if (q_obs == nullptr) return SS_ERR_INVALID_ARG;
     if (cfg->W > L || cfg->W > cfg->L_recent) return SS_ERR_INVALID_ARG;
+    if (lse_call && (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3) != 0))
+      return SS_ERR_INVALID_ARG;
   }
   const PrefillPlan p = plan_prefill(cfg, b, L);
   if (ws == nullptr || ws_bytes < (compressed ? p.total : ALIGN)) return SS_ERR_WORKSPACE;
@@ -230,6 +235,7 @@ ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, c
     a.n_chunk1 = p.n_chunk1;
     a.chunk2 = p.chunk2;
     a.n_chunk2 = p.n_chunk2;
+    a.lse = lse_call ? lse : nullptr;
     a.part1 = reinterpret_cast<float*>(w + p.off_part1);
     a.rowstat = reinterpret_cast<float*>(w + p.off_rowstat);
     a.raw = raw_out ? raw_out : reinterpret_cast<float*>(w + p.off_raw);
@@ -311,8 +317,8 @@ ss_status ss_prefill_compress(const ss_config* cfg, const void* q_obs, const voi
                               const void* v, int32_t b, int32_t L, const int32_t* rows,
                               const ss_cache* cache, float* raw_out, float* pooled_out,
                               int32_t* sel_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return prefill_impl(cfg, q_obs, k, v, b, L, rows, cache, raw_out, pooled_out, sel_out, ws,
-                      ws_bytes, stream, nullptr, nullptr);
+  return prefill_impl(cfg, q_obs, k, v, b, L, false, nullptr, rows, cache, raw_out, pooled_out,
+                      sel_out, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
 ss_status ss_prefill_compress_timed(const ss_config* cfg, const void* q_obs, const void* k,
@@ -320,8 +326,28 @@ ss_status ss_prefill_compress_timed(const ss_config* cfg, const void* q_obs, con
                                     const ss_cache* cache, float* raw_out, float* pooled_out,
                                     int32_t* sel_out, void* ws, size_t ws_bytes,
                                     hipStream_t stream, hipEvent_t begin, hipEvent_t end) {
-  return prefill_impl(cfg, q_obs, k, v, b, L, rows, cache, raw_out, pooled_out, sel_out, ws,
-                      ws_bytes, stream, begin, end);
+  return prefill_impl(cfg, q_obs, k, v, b, L, false, nullptr, rows, cache, raw_out, pooled_out,
+                      sel_out, ws, ws_bytes, stream, begin, end);
+}
+
+ss_status ss_prefill_compress_lse(const ss_config* cfg, const void* q_obs, const void* k,
+                                  const void* v, int32_t b, int32_t L, const float* lse_obs,
+                                  const int32_t* rows, const ss_cache* cache, float* raw_out,
+                                  float* pooled_out, int32_t* sel_out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  return prefill_impl(cfg, q_obs, k, v, b, L, true, lse_obs, rows, cache, raw_out, pooled_out,
+                      sel_out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+ss_status ss_prefill_compress_lse_timed(const ss_config* cfg, const void* q_obs, const void* k,
+                                        const void* v, int32_t b, int32_t L,
+                                        const float* lse_obs, const int32_t* rows,
+                                        const ss_cache* cache, float* raw_out,
+                                        float* pooled_out, int32_t* sel_out, void* ws,
+                                        size_t ws_bytes, hipStream_t stream, hipEvent_t begin,
+                                        hipEvent_t end) {
+  return prefill_impl(cfg, q_obs, k, v, b, L, true, lse_obs, rows, cache, raw_out, pooled_out,
+                      sel_out, ws, ws_bytes, stream, begin, end);
 }
 
 ss_status ss_decode_step(const ss_config* cfg, const void* q, const void* k_new,

@@ -41,6 +41,7 @@ struct PrefillArgs {
   void* vc;              // cache v or null
   int32_t* slot_pos;
   int32_t* n_tokens;
+  const float* lse;      // [b, Hq, W] given row log-sum-exp (natural log) or null
   float* part1;          // ws: [b, Hkv, Rg, n_chunk1, 2] per-chunk (max, sum)
   float* rowstat;        // ws: [b, Hkv, Rg, 2] (max, 1/sum)
   float* raw;            // [b, Hkv, m]

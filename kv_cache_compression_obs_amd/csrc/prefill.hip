@@ -189,6 +189,27 @@ __global__ __launch_bounds__(256) void score_rowstat_combine_kernel(PrefillArgs 
   a.rowstat[2 * idx + 1] = S > 0.0 ? static_cast<float>(1.0 / S) : 0.f;
 }
 
+// Row statistics from a given log-sum-exp instead of pass 1.  With lse in
+// natural-log units, p = exp(z - lse) = 2^(x - lse*log2(e)); the row keeps
+// M = fp32(lse*log2(e)) and the weight w = 2^(M - lse*log2(e)) (both from
+// fp64), so p = 2^(x - M) * w carries the given lse to fp32 accuracy whatever
+// its magnitude.
+__global__ __launch_bounds__(256) void lse_rowstat_kernel(PrefillArgs a) {
+  const size_t n = static_cast<size_t>(a.b) * a.Hkv * a.Rg;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int row = static_cast<int>(idx % a.Rg);
+  const size_t gidx = idx / a.Rg;  // (request, kv-head)
+  if (row >= a.G * a.W) return;    // padding rows are never read
+  const size_t bi = gidx / a.Hkv, h = gidx % a.Hkv;
+  // q-heads h*G .. h*G+G-1 of request bi, W rows each, contiguous: row = g*W + r
+  const double l2 = static_cast<double>(a.lse[(bi * a.Hq + h * a.G) * a.W + row]) *
+                    1.4426950408889634074;
+  const float M = static_cast<float>(l2);
+  a.rowstat[2 * idx] = M;
+  a.rowstat[2 * idx + 1] = static_cast<float>(exp2(static_cast<double>(M) - l2));
+}
+
 // Pass 2.  Grid (n_chunk2, Hkv, b) over the middle keys [S, L-R).  Every
 // middle key is visible to every observation row (the window lies inside the
 // recent region), so no causal mask.  Column sums: 4 rows in registers, then
@@ -324,10 +345,14 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
 template <typename T, int D, int KT, int NWV>
 hipError_t run_scores_w(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
-  score_rowstat_kernel<T, D, KT, NWV><<<dim3(a.n_chunk1, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
   const size_t rows = static_cast<size_t>(a.b) * a.Hkv * a.Rg;
-  score_rowstat_combine_kernel<<<static_cast<unsigned>(cdiv(static_cast<int>(rows), 256)), 256, 0,
-                                 st>>>(a);
+  const unsigned rgrid = static_cast<unsigned>(cdiv(static_cast<int>(rows), 256));
+  if (a.lse != nullptr) {
+    lse_rowstat_kernel<<<rgrid, 256, 0, st>>>(a);
+  } else {
+    score_rowstat_kernel<T, D, KT, NWV><<<dim3(a.n_chunk1, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
+    score_rowstat_combine_kernel<<<rgrid, 256, 0, st>>>(a);
+  }
   score_columns_kernel<T, D, KT, NWV><<<dim3(a.n_chunk2, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();

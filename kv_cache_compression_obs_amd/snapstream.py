@@ -20,7 +20,8 @@ TORCH_DTYPE = {SS_F32: torch.float32, SS_BF16: torch.bfloat16}
 
 EXPORTS = ("ss_cache_slots", "ss_prefill_workspace_bytes", "ss_decode_workspace_bytes",
            "ss_decode_workspace_init", "ss_prefill_compress", "ss_decode_step",
-           "ss_prefill_compress_timed", "ss_decode_step_timed", "ss_status_string")
+           "ss_prefill_compress_timed", "ss_decode_step_timed", "ss_prefill_compress_lse",
+           "ss_prefill_compress_lse_timed", "ss_status_string")
 
 
 class ss_config(ctypes.Structure):
@@ -76,6 +77,11 @@ def lib() -> ctypes.CDLL:
         L.ss_prefill_compress_timed.restype = I32
         L.ss_decode_step_timed.argtypes = L.ss_decode_step.argtypes + [VP, VP]
         L.ss_decode_step_timed.restype = I32
+        L.ss_prefill_compress_lse.argtypes = [P(ss_config), VP, VP, VP, I32, I32, VP, VP,
+                                              P(ss_cache), VP, VP, VP, VP, SZ, VP]
+        L.ss_prefill_compress_lse.restype = I32
+        L.ss_prefill_compress_lse_timed.argtypes = L.ss_prefill_compress_lse.argtypes + [VP, VP]
+        L.ss_prefill_compress_lse_timed.restype = I32
         L.ss_decode_workspace_init.argtypes = [P(ss_config), I32, VP, SZ, VP]
         L.ss_decode_workspace_init.restype = I32
         L.ss_status_string.argtypes = [I32]
@@ -172,10 +178,12 @@ class Cache:
 
 def ss_prefill_compress(cfg: ss_config, q_obs, k, v, cache: Cache, rows=None, raw_out=None,
                         pooled_out=None, sel_out=None, ws=None, stream=None,
-                        events=None) -> None:
+                        events=None, lse=None) -> None:
     """Build the fixed cache of b = k.shape[0] requests of L = k.shape[2] tokens
     into `cache` (rows `rows`, default 0..b-1).  events: optional pair of raw
-    hipEvent_t handles recorded around the score kernels."""
+    hipEvent_t handles recorded around the score kernels.  lse: optional
+    float32 [b, n_q_heads, W] log-sum-exp of the observation rows; given, the
+    call goes to ss_prefill_compress_lse (one score pass)."""
     dt = TORCH_DTYPE[cfg.dtype]
     for t, n in ((q_obs, "q_obs"), (k, "k"), (v, "v")):
         _check(t, n, dt)
@@ -188,14 +196,20 @@ def ss_prefill_compress(cfg: ss_config, q_obs, k, v, cache: Cache, rows=None, ra
         ws = torch.empty(ss_prefill_workspace_bytes(cfg, b, L), dtype=torch.uint8,
                          device=k.device)
     cs = cache.struct()
-    args = (ctypes.byref(cfg), _ptr(q_obs), _ptr(k), _ptr(v), b, L, _ptr(rows), ctypes.byref(cs),
-            _ptr(raw_out), _ptr(pooled_out), _ptr(sel_out), _ptr(ws), ws.numel(), _stream(stream))
-    if events is None:
-        st = lib().ss_prefill_compress(*args)
+    tail = (_ptr(rows), ctypes.byref(cs), _ptr(raw_out), _ptr(pooled_out), _ptr(sel_out),
+            _ptr(ws), ws.numel(), _stream(stream))
+    head = (ctypes.byref(cfg), _ptr(q_obs), _ptr(k), _ptr(v), b, L)
+    if lse is not None:
+        _check(lse, "lse", torch.float32)
+        args, name = head + (_ptr(lse),) + tail, "ss_prefill_compress_lse"
     else:
-        st = lib().ss_prefill_compress_timed(*args, events[0], events[1])
+        args, name = head + tail, "ss_prefill_compress"
+    if events is None:
+        st = getattr(lib(), name)(*args)
+    else:
+        st = getattr(lib(), name + "_timed")(*args, events[0], events[1])
     if st != SS_OK:
-        raise SnapStreamError(st, "ss_prefill_compress")
+        raise SnapStreamError(st, name)
 
 
 def ss_decode_step(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, out, err_flag=None,

@@ -12,6 +12,8 @@ Comparison rules:
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -56,9 +58,30 @@ def compare_selection(gpu_sel, pooled, oracle_sel, K):
     return int(band.sum()), swaps
 
 
-def run_lib_prefill(w, inp, cache=None, rows=None, B_max=None):
+def lse_obs(w, inp, device="cuda"):
+    """Natural-log log-sum-exp of every observation row over its causal keys,
+    in fp64 (torch.logsumexp) from the stored input values, returned as the
+    float32 [b, Hq, W] device tensor a prefill attention would hand over."""
+    q, k = inp["q_obs"], inp["k"]
+    b, Hq, W, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    scale = w.get("scale", 0.0) or 1.0 / math.sqrt(d)
+    vis = torch.arange(L, device=device)[None, :] <= (L - W + torch.arange(W, device=device))[:, None]
+    out = torch.empty(b, Hq, W, dtype=torch.float64, device=device)
+    for bi in range(b):
+        for h in range(Hkv):
+            kt = k[bi, h].to(device, torch.float64).t().contiguous()        # [d, L]
+            for g in range(G):
+                z = scale * (q[bi, h * G + g].to(device, torch.float64) @ kt)  # [W, L]
+                out[bi, h * G + g] = torch.logsumexp(z.masked_fill(~vis, -math.inf), dim=1)
+    return out.float().contiguous()
+
+
+def run_lib_prefill(w, inp, cache=None, rows=None, B_max=None, lse=None):
     """Library prefill of the whole batch; returns (cache, raw, pooled, sel) with
-    the stage outputs as CPU numpy arrays (None when L <= C)."""
+    the stage outputs as CPU numpy arrays (None when L <= C).  lse: the
+    observation rows' log-sum-exp (one-pass scoring entry point)."""
     cfg = lib_config(w)
     k = inp["k"]
     b, Hkv, L = k.shape[0], k.shape[1], k.shape[2]
@@ -72,7 +95,7 @@ def run_lib_prefill(w, inp, cache=None, rows=None, B_max=None):
         pooled = torch.full((b, Hkv, m), float("nan"), device="cuda")
         sel = torch.full((b, Hkv, max(w["K"], 1)), -7, dtype=torch.int32, device="cuda")[..., :w["K"]].contiguous()
     ss.ss_prefill_compress(cfg, inp["q_obs"], k, inp["v"], cache, rows=rows, raw_out=raw,
-                           pooled_out=pooled, sel_out=sel)
+                           pooled_out=pooled, sel_out=sel, lse=lse)
     torch.cuda.synchronize()
     cpu = lambda t: None if t is None else t.cpu().numpy()  # noqa: E731
     return cache, cpu(raw), cpu(pooled), cpu(sel)
@@ -153,12 +176,15 @@ def pool_exact(x, P):
     return np.lib.stride_tricks.sliding_window_view(pad, P).max(axis=1)
 
 
-def prefill_case(w, seed, B=None, L=None, groups=None, device="cuda", raw_rtol=2e-5):
-    say(f"prefill {w['name']} dtype={w['dtype']} d={w['d_qk']} B={B or w['B']} L={L or w['L']}")
+def prefill_case(w, seed, B=None, L=None, groups=None, device="cuda", raw_rtol=2e-5,
+                 given_lse=False):
+    """given_lse: score through the one-pass entry point, fed with lse_obs."""
+    say(f"prefill {w['name']} dtype={w['dtype']} d={w['d_qk']} B={B or w['B']} L={L or w['L']}"
+        + (" (given lse)" if given_lse else ""))
     inp = synth.prefill_inputs(w, seed, device=device, B=B, L=L)
     if device != "cuda":
         inp = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
-    res = run_lib_prefill(w, inp)
+    res = run_lib_prefill(w, inp, lse=lse_obs(w, inp) if given_lse else None)
     Bn, Hkv = inp["k"].shape[0], inp["k"].shape[1]
     groups = groups or [(b, h) for b in range(Bn) for h in range(Hkv)]
     worst = {}

@@ -133,6 +133,13 @@ def test_null_pointers_and_small_workspace_are_rejected():
     assert lib.ss_prefill_compress(ctypes.byref(bad), fake, fake, fake, 2, 16384, None,
                                    ctypes.byref(cache), None, None, None, fake, 1 << 40,
                                    None) in (ss.SS_ERR_INVALID_ARG, ss.SS_ERR_UNSUPPORTED)
+    # the one-pass entry point needs the rows' log-sum-exp when it compresses
+    assert lib.ss_prefill_compress_lse(ctypes.byref(cfg), fake, fake, fake, 2, 16384, None, None,
+                                       ctypes.byref(cache), None, None, None, fake, 1 << 40,
+                                       None) == ss.SS_ERR_INVALID_ARG
+    assert lib.ss_prefill_compress_lse(ctypes.byref(cfg), fake, fake, fake, 2, 16384,
+                                       ctypes.c_void_p(0x1002), None, ctypes.byref(cache), None,
+                                       None, None, fake, 1 << 40, None) == ss.SS_ERR_INVALID_ARG
     # a tensor pointer off the 16-byte grid
     odd = ctypes.c_void_p(0x1008)
     assert lib.ss_decode_step(ctypes.byref(cfg), odd, fake, fake, fake, ctypes.byref(cache), fake,

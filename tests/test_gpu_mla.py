@@ -29,6 +29,10 @@ def test_mla_prefill_small_ragged():
     prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512), 21, L=4999)
 
 
+def test_mla_prefill_given_lse_one_pass():
+    prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512), 29, L=4999, given_lse=True)
+
+
 def test_mla_prefill_uncompressed_is_identity():
     prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512), 22, L=700)
 

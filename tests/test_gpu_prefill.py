@@ -55,3 +55,18 @@ def test_prefill_llama8b_128k_sampled_groups():
     # 8 requests x 8 kv-heads, 131072 -> 32768 on the GPU; the oracle checks
     # three (request, kv-head) groups one by one
     prefill_case(synth.workload("llama8b_128k"), 12, groups=[(0, 0), (3, 5), (7, 7)])
+
+
+@pytest.mark.parametrize("name,L,kw", [
+    ("tiny_fp32", None, {}),
+    ("llama8b_c4k", 4999, dict(B=2, L_sink=16, K=200, L_recent=512)),
+])
+def test_prefill_given_lse_one_pass(name, L, kw):
+    # the observation rows' log-sum-exp handed over (as a prefill attention
+    # returns it): the scores come from one pass over the middle keys and
+    # must meet the same bar as the two-pass scoring
+    prefill_case(synth.workload(name, **kw), 41, L=L, given_lse=True)
+
+
+def test_prefill_given_lse_llama8b_128k_sampled_groups():
+    prefill_case(synth.workload("llama8b_128k"), 42, groups=[(0, 0), (5, 3)], given_lse=True)
