@@ -188,6 +188,49 @@ def given_lse_prefill(ss, torch, w, cfg, inp, reps=5):
                     "log-sum-exp given"}
 
 
+def varlen_admission(ss, torch, synth, w, cfg, reps=5):
+    """Continuous-batching admission of B prompts of log-uniform lengths in
+    [1024, L] (seeded): one ss_prefill_compress_varlen call against one
+    ss_prefill_compress call per request."""
+    B = w["B"]
+    lens = synth.request_lengths(dict(w, len_min=min(1024, w["L"]), len_max=w["L"]), 3, B)
+    reqs = [synth.prefill_inputs(w, 300 + i, device="cuda", B=1, L=n) for i, n in enumerate(lens)]
+    q_obs = torch.cat([r["q_obs"] for r in reqs]).contiguous()
+    k = torch.cat([r["k"][0] for r in reqs], dim=1).contiguous()
+    v = (torch.cat([r["v"][0] for r in reqs], dim=1).contiguous()
+         if reqs[0]["v"] is not None else None)
+    cu = torch.tensor([0] + [sum(lens[:i + 1]) for i in range(B)], dtype=torch.int32,
+                      device="cuda")
+    max_L = max(lens)
+    cache = ss.Cache(cfg, B)
+    ws = torch.empty(ss.ss_prefill_workspace_bytes(cfg, B, max_L), dtype=torch.uint8,
+                     device="cuda")
+    rows = [torch.tensor([i], dtype=torch.int32, device="cuda") for i in range(B)]
+
+    def one_call():
+        ss.ss_prefill_compress_varlen(cfg, q_obs, k, v, cu, max_L, cache, ws=ws)
+
+    def per_request():
+        for i, r in enumerate(reqs):
+            ss.ss_prefill_compress(cfg, r["q_obs"], r["k"], r["v"], cache, rows=rows[i], ws=ws)
+
+    out = {}
+    for name, fn in (("one_call_ms", one_call), ("per_request_calls_ms", per_request)):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        out[name] = round(ev[0].elapsed_time(ev[1]) / reps, 4)
+    out.update(requests=B, compressed=sum(n > w["C"] for n in lens),
+               length_range=[min(lens), max(lens)],
+               speedup=round(out["per_request_calls_ms"] / out["one_call_ms"], 3))
+    return out
+
+
 def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_s):
     """The same decode over a cache that keeps the whole prompt (C = L: the
     recent window widened to L - L_sink - K, so the prompt is stored as it is
@@ -381,6 +424,7 @@ def main():
         },
     }
     res["given_lse"] = given_lse_prefill(ss, torch, w, cfg, inp)
+    res["varlen_admission"] = varlen_admission(ss, torch, synth, w, cfg)
     if not args.no_uncompressed:
         caches.clear()                      # frees the compressed copies
         res["uncompressed_baseline"] = uncompressed_baseline(

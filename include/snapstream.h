@@ -167,6 +167,37 @@ ss_status ss_prefill_compress_lse(const ss_config* cfg, const void* q_obs, const
                                   float* pooled_out, int32_t* sel_out, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
+/* ss_prefill_compress for a batch of prompts of different lengths in one
+ * call (continuous-batching admissions: "Why This Wasn't Already Standard",
+ * requests at different points of their life share one static batch).
+ *
+ *   k, v        packed per kv-head: [n_kv_heads, T, d_qk] / [n_kv_heads, T, d_v]
+ *               (v NULL when v_aliases_k), where request i holds tokens
+ *               cu_seqlens[i] .. cu_seqlens[i+1]-1 of every head, T = cu_seqlens[b]
+ *   cu_seqlens  device int32 [b+1], non-decreasing, cu_seqlens[0] = 0
+ *   max_L       host bound on every prompt length L_i = cu_seqlens[i+1] -
+ *               cu_seqlens[i]; it sizes the launch and the workspace
+ *               (ss_prefill_workspace_bytes(cfg, b, max_L))
+ *   q_obs       [b, n_q_heads, W, d_qk]: the last W queries of each request
+ *               (read only for requests with L_i > C)
+ *   lse_obs     optional device float [b, n_q_heads, W]: given, the scoring
+ *               makes one pass as in ss_prefill_compress_lse; NULL: two passes
+ *   raw_out / pooled_out  optional [b, n_kv_heads, max_L - L_sink - L_recent];
+ *               request i fills its first L_i - L_sink - L_recent entries
+ *   sel_out     optional [b, n_kv_heads, K]
+ *
+ * Request i is stored uncompressed when L_i <= C and compressed otherwise,
+ * exactly as a single-request ss_prefill_compress of its L_i tokens would
+ * store it; n_tokens[row] = L_i.  A request whose offsets are not
+ * non-decreasing within [0, T], or longer than max_L, is stored as empty
+ * (every slot -1, n_tokens 0). */
+ss_status ss_prefill_compress_varlen(const ss_config* cfg, const void* q_obs, const void* k,
+                                     const void* v, int32_t b, const int32_t* cu_seqlens,
+                                     int32_t max_L, const float* lse_obs, const int32_t* rows,
+                                     const ss_cache* cache, float* raw_out, float* pooled_out,
+                                     int32_t* sel_out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
 /* One decode step of every cache row ("Ring Buffer vs. Naive Slicing": write
  * the new key/value into its fixed ring slot, evicting position pos -
  * L_recent; then memory-bound attention over the fixed cache).
@@ -212,6 +243,14 @@ ss_status ss_prefill_compress_lse_timed(const ss_config* cfg, const void* q_obs,
                                         float* pooled_out, int32_t* sel_out, void* ws,
                                         size_t ws_bytes, hipStream_t stream, hipEvent_t begin,
                                         hipEvent_t end);
+ss_status ss_prefill_compress_varlen_timed(const ss_config* cfg, const void* q_obs,
+                                           const void* k, const void* v, int32_t b,
+                                           const int32_t* cu_seqlens, int32_t max_L,
+                                           const float* lse_obs, const int32_t* rows,
+                                           const ss_cache* cache, float* raw_out,
+                                           float* pooled_out, int32_t* sel_out, void* ws,
+                                           size_t ws_bytes, hipStream_t stream,
+                                           hipEvent_t begin, hipEvent_t end);
 ss_status ss_decode_step_timed(const ss_config* cfg, const void* q, const void* k_new,
                                const void* v_new, const int32_t* pos, const ss_cache* cache,
                                void* out, int32_t* err_flag, void* ws, size_t ws_bytes,

@@ -177,11 +177,12 @@ ss_status ss_decode_workspace_init(const ss_config* cfg, int32_t B_max, void* ws
 
 namespace {
 
-// lse_call: the ss_prefill_compress_lse entry points (the row log-sum-exp is
-// given; required when the prompt is compressed).
+// lse_call: the row log-sum-exp is given (required when a prompt is
+// compressed).  cu: request token offsets of a packed varlen batch (device,
+// [b+1]); L is then the longest prompt allowed.
 ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, const void* v,
                        int32_t b, int32_t L, bool lse_call, const float* lse,
-                       const int32_t* rows, const ss_cache* cache,
+                       const int32_t* cu, const int32_t* rows, const ss_cache* cache,
                        float* raw_out, float* pooled_out, int32_t* sel_out, void* ws,
                        size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const ss_status cs = check_config(cfg);
@@ -194,8 +195,9 @@ ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, c
       misaligned(cache->v) || misaligned(ws))
     return SS_ERR_INVALID_ARG;
   if (rows == nullptr && b > cache->B_max) return SS_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(cu) & 3) != 0) return SS_ERR_INVALID_ARG;
   const int C = cache_slots(cfg);
-  const bool compressed = L > C;
+  const bool compressed = L > C;  // with cu: some request may be compressed
   if (compressed) {
     if (q_obs == nullptr) return SS_ERR_INVALID_ARG;
     if (cfg->W > L || cfg->W > cfg->L_recent) return SS_ERR_INVALID_ARG;
@@ -227,6 +229,7 @@ ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, c
   a.R = cfg->L_recent;
   a.pool = cfg->pool;
   a.scale_log2 = scale_log2(cfg);
+  a.cu = cu;
   if (compressed) {
     char* w = static_cast<char*>(ws);
     a.m = p.m;
@@ -317,8 +320,8 @@ ss_status ss_prefill_compress(const ss_config* cfg, const void* q_obs, const voi
                               const void* v, int32_t b, int32_t L, const int32_t* rows,
                               const ss_cache* cache, float* raw_out, float* pooled_out,
                               int32_t* sel_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return prefill_impl(cfg, q_obs, k, v, b, L, false, nullptr, rows, cache, raw_out, pooled_out,
-                      sel_out, ws, ws_bytes, stream, nullptr, nullptr);
+  return prefill_impl(cfg, q_obs, k, v, b, L, false, nullptr, nullptr, rows, cache, raw_out,
+                      pooled_out, sel_out, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
 ss_status ss_prefill_compress_timed(const ss_config* cfg, const void* q_obs, const void* k,
@@ -326,8 +329,8 @@ ss_status ss_prefill_compress_timed(const ss_config* cfg, const void* q_obs, con
                                     const ss_cache* cache, float* raw_out, float* pooled_out,
                                     int32_t* sel_out, void* ws, size_t ws_bytes,
                                     hipStream_t stream, hipEvent_t begin, hipEvent_t end) {
-  return prefill_impl(cfg, q_obs, k, v, b, L, false, nullptr, rows, cache, raw_out, pooled_out,
-                      sel_out, ws, ws_bytes, stream, begin, end);
+  return prefill_impl(cfg, q_obs, k, v, b, L, false, nullptr, nullptr, rows, cache, raw_out,
+                      pooled_out, sel_out, ws, ws_bytes, stream, begin, end);
 }
 
 ss_status ss_prefill_compress_lse(const ss_config* cfg, const void* q_obs, const void* k,
@@ -335,8 +338,8 @@ ss_status ss_prefill_compress_lse(const ss_config* cfg, const void* q_obs, const
                                   const int32_t* rows, const ss_cache* cache, float* raw_out,
                                   float* pooled_out, int32_t* sel_out, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
-  return prefill_impl(cfg, q_obs, k, v, b, L, true, lse_obs, rows, cache, raw_out, pooled_out,
-                      sel_out, ws, ws_bytes, stream, nullptr, nullptr);
+  return prefill_impl(cfg, q_obs, k, v, b, L, true, lse_obs, nullptr, rows, cache, raw_out,
+                      pooled_out, sel_out, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
 ss_status ss_prefill_compress_lse_timed(const ss_config* cfg, const void* q_obs, const void* k,
@@ -346,8 +349,33 @@ ss_status ss_prefill_compress_lse_timed(const ss_config* cfg, const void* q_obs,
                                         float* pooled_out, int32_t* sel_out, void* ws,
                                         size_t ws_bytes, hipStream_t stream, hipEvent_t begin,
                                         hipEvent_t end) {
-  return prefill_impl(cfg, q_obs, k, v, b, L, true, lse_obs, rows, cache, raw_out, pooled_out,
-                      sel_out, ws, ws_bytes, stream, begin, end);
+  return prefill_impl(cfg, q_obs, k, v, b, L, true, lse_obs, nullptr, rows, cache, raw_out,
+                      pooled_out, sel_out, ws, ws_bytes, stream, begin, end);
+}
+
+ss_status ss_prefill_compress_varlen(const ss_config* cfg, const void* q_obs, const void* k,
+                                     const void* v, int32_t b, const int32_t* cu_seqlens,
+                                     int32_t max_L, const float* lse_obs, const int32_t* rows,
+                                     const ss_cache* cache, float* raw_out, float* pooled_out,
+                                     int32_t* sel_out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (cu_seqlens == nullptr) return SS_ERR_INVALID_ARG;
+  return prefill_impl(cfg, q_obs, k, v, b, max_L, lse_obs != nullptr, lse_obs, cu_seqlens, rows,
+                      cache, raw_out, pooled_out, sel_out, ws, ws_bytes, stream, nullptr,
+                      nullptr);
+}
+
+ss_status ss_prefill_compress_varlen_timed(const ss_config* cfg, const void* q_obs,
+                                           const void* k, const void* v, int32_t b,
+                                           const int32_t* cu_seqlens, int32_t max_L,
+                                           const float* lse_obs, const int32_t* rows,
+                                           const ss_cache* cache, float* raw_out,
+                                           float* pooled_out, int32_t* sel_out, void* ws,
+                                           size_t ws_bytes, hipStream_t stream,
+                                           hipEvent_t begin, hipEvent_t end) {
+  if (cu_seqlens == nullptr) return SS_ERR_INVALID_ARG;
+  return prefill_impl(cfg, q_obs, k, v, b, max_L, lse_obs != nullptr, lse_obs, cu_seqlens, rows,
+                      cache, raw_out, pooled_out, sel_out, ws, ws_bytes, stream, begin, end);
 }
 
 ss_status ss_decode_step(const ss_config* cfg, const void* q, const void* k_new,

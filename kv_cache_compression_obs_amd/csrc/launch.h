@@ -42,6 +42,7 @@ struct PrefillArgs {
   int32_t* slot_pos;
   int32_t* n_tokens;
   const float* lse;      // [b, Hq, W] given row log-sum-exp (natural log) or null
+  const int32_t* cu;     // [b+1] request token offsets (packed [Hkv, cu[b], d] keys) or null
   float* part1;          // ws: [b, Hkv, Rg, n_chunk1, 2] per-chunk (max, sum)
   float* rowstat;        // ws: [b, Hkv, Rg, 2] (max, 1/sum)
   float* raw;            // [b, Hkv, m]
@@ -53,6 +54,22 @@ struct PrefillArgs {
   int chunk2, n_chunk2;  // middle keys per column-score workgroup, count
   float scale_log2;
 };
+
+// The prompt of request bi: its length and the row of k (and of v) that
+// holds its first token for kv-head h.  Without `cu` every request has a.L
+// tokens in [b, Hkv, L, d] layout; with `cu` the requests are packed per
+// kv-head ([Hkv, cu[b], d]) and a.L is the longest allowed.  Offsets that are
+// not non-decreasing, or a request longer than a.L, make that request empty.
+struct Prompt {
+  int L;
+  size_t row0;
+};
+__device__ __forceinline__ Prompt prompt_of(const PrefillArgs& a, int bi, int h) {
+  if (a.cu == nullptr) return {a.L, (static_cast<size_t>(bi) * a.Hkv + h) * a.L};
+  const int c0 = a.cu[bi], c1 = a.cu[bi + 1], T = a.cu[a.b];
+  const bool ok = c0 >= 0 && c0 <= c1 && c1 <= T && c1 - c0 <= a.L;
+  return {ok ? c1 - c0 : 0, static_cast<size_t>(h) * T + (ok ? c0 : 0)};
+}
 
 // Returns hipErrorInvalidValue when no kernel exists for (dtype, D, DV).
 // ev0/ev1 (nullable) are recorded right before/after the dominant kernels.

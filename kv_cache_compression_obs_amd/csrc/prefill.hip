@@ -93,6 +93,8 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
   const int col = lane & 15, qg = lane >> 4;
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const bool active = 16 * wave < a.G * a.W;  // wave-uniform
+  const Prompt pr = prompt_of(a, bi, h);
+  if (pr.L <= a.C || chunk * a.chunk1 >= pr.L) return;  // stored as is / past the prompt
 
   typename MM::frag qf[NC];
   load_q<T, D>(qf, a, bi, h, 16 * wave + col, qg);
@@ -100,10 +102,10 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 16 * wave + 4 * qg + r;
-    lim[r] = row < a.G * a.W ? a.L - a.W + row % a.W : -1;  // last visible key
+    lim[r] = row < a.G * a.W ? pr.L - a.W + row % a.W : -1;  // last visible key
   }
-  const int k0 = chunk * a.chunk1, k1 = min(k0 + a.chunk1, a.L);
-  const T* kbase = static_cast<const T*>(a.k) + (static_cast<size_t>(bi) * a.Hkv + h) * a.L * D;
+  const int k0 = chunk * a.chunk1, k1 = min(k0 + a.chunk1, pr.L);
+  const T* kbase = static_cast<const T*>(a.k) + pr.row0 * D;
 
   float m[4], s[4];
 #pragma unroll
@@ -177,12 +179,16 @@ __global__ __launch_bounds__(256) void score_rowstat_combine_kernel(PrefillArgs 
   const size_t n = static_cast<size_t>(a.b) * a.Hkv * a.Rg;
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n) return;
+  const size_t gidx = idx / a.Rg;
+  const Prompt pr = prompt_of(a, static_cast<int>(gidx / a.Hkv), static_cast<int>(gidx % a.Hkv));
+  if (pr.L <= a.C) return;
+  const int nc = cdiv(pr.L, a.chunk1);  // chunks pass 1 wrote for this request
   const float* p = a.part1 + 2 * idx * a.n_chunk1;
   float M = -INFINITY;
-  for (int c = 0; c < a.n_chunk1; ++c) M = fmaxf(M, p[2 * c]);
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, p[2 * c]);
   double S = 0.0;
   if (M != -INFINITY)
-    for (int c = 0; c < a.n_chunk1; ++c)
+    for (int c = 0; c < nc; ++c)
       if (p[2 * c] != -INFINITY)
         S += static_cast<double>(p[2 * c + 1]) * exp2(static_cast<double>(p[2 * c]) - M);
   a.rowstat[2 * idx] = M;
@@ -202,6 +208,7 @@ __global__ __launch_bounds__(256) void lse_rowstat_kernel(PrefillArgs a) {
   const size_t gidx = idx / a.Rg;  // (request, kv-head)
   if (row >= a.G * a.W) return;    // padding rows are never read
   const size_t bi = gidx / a.Hkv, h = gidx % a.Hkv;
+  if (prompt_of(a, static_cast<int>(bi), static_cast<int>(h)).L <= a.C) return;
   // q-heads h*G .. h*G+G-1 of request bi, W rows each, contiguous: row = g*W + r
   const double l2 = static_cast<double>(a.lse[(bi * a.Hq + h * a.G) * a.W + row]) *
                     1.4426950408889634074;
@@ -241,9 +248,11 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
     M[r] = ok[r] ? a.rowstat[2 * (gidx * a.Rg + row)] : 0.f;
     w[r] = ok[r] ? a.rowstat[2 * (gidx * a.Rg + row) + 1] : 0.f;
   }
-  const int mend = a.L - a.R;
+  const Prompt pr = prompt_of(a, bi, h);
+  const int mend = pr.L - a.R;
   const int k0 = a.S + chunk * a.chunk2, k1 = min(k0 + a.chunk2, mend);
-  const T* kbase = static_cast<const T*>(a.k) + gidx * a.L * D;
+  if (pr.L <= a.C || k0 >= k1) return;  // stored as is / past the middle region
+  const T* kbase = static_cast<const T*>(a.k) + pr.row0 * D;
   float* raw = a.raw + gidx * a.m - a.S;  // indexed by absolute key
 
   u32x4_t ld[KTile::NLD];
@@ -297,29 +306,32 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
   if (row < 0 || row >= a.B_max) return;  // rows outside the cache are ignored
   const size_t gsrc = static_cast<size_t>(bi) * a.Hkv + h;
   const size_t gdst = static_cast<size_t>(row) * a.Hkv + h;
+  const Prompt pr = prompt_of(a, bi, h);
+  const int L = pr.L;
+  const bool cmp = a.cu != nullptr ? L > a.C : compressed != 0;
   if (tid < SLOTS) {
     const int s = sb * SLOTS + tid;
     int t = -1;
     if (s < a.C) {
-      if (!compressed) {
-        t = s < a.L ? s : -1;
+      if (!cmp) {
+        t = s < L ? s : -1;
       } else if (s < a.S) {
         t = s;
       } else if (s < a.S + a.K) {
         const int j = a.sel[gsrc * a.K + (s - a.S)];
-        t = (j >= 0 && j < a.m) ? a.S + j : -1;
+        t = (j >= 0 && j < L - a.S - a.R) ? a.S + j : -1;
       } else {
-        int r = (s - a.L) % a.R;
+        int r = (s - L) % a.R;
         if (r < 0) r += a.R;
-        t = a.L - a.R + r;
+        t = L - a.R + r;
       }
       a.slot_pos[gdst * a.C + s] = t;
     }
     tok[tid] = t;
   }
-  if (sb == 0 && h == 0 && tid == 0) a.n_tokens[row] = a.L;
+  if (sb == 0 && h == 0 && tid == 0) a.n_tokens[row] = L;
   __syncthreads();
-  const char* ksrc = reinterpret_cast<const char*>(static_cast<const T*>(a.k) + gsrc * a.L * D);
+  const char* ksrc = reinterpret_cast<const char*>(static_cast<const T*>(a.k) + pr.row0 * D);
   char* kdst = reinterpret_cast<char*>(static_cast<T*>(a.kc) + gdst * a.C * D);
   for (int id = tid; id < SLOTS * KCH; id += blockDim.x) {
     const int j = id / KCH, ch = id % KCH;
@@ -330,7 +342,7 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
         *reinterpret_cast<const u32x4_t*>(ksrc + static_cast<size_t>(t) * KCH * 16 + ch * 16);
   }
   if (ALIAS) return;
-  const char* vsrc = reinterpret_cast<const char*>(static_cast<const T*>(a.v) + gsrc * a.L * DV);
+  const char* vsrc = reinterpret_cast<const char*>(static_cast<const T*>(a.v) + pr.row0 * DV);
   char* vdst = reinterpret_cast<char*>(static_cast<T*>(a.vc) + gdst * a.C * DV);
   for (int id = tid; id < SLOTS * VCH; id += blockDim.x) {
     const int j = id / VCH, ch = id % VCH;

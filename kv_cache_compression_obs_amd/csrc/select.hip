@@ -78,9 +78,12 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, bi = blockIdx.y;
   const size_t g = static_cast<size_t>(bi) * a.Hkv + h;
-  const int m = a.m, p = (a.pool - 1) / 2, K = a.K;
-  const float* raw = a.raw + g * m;
-  float* pooled = a.pooled + g * m;
+  const int L = prompt_of(a, bi, h).L;
+  if (L <= a.C) return;  // stored as is: nothing to select
+  // m: this request's middle keys; a.m: the row stride of raw / pooled / sel
+  const int m = L - a.S - a.R, p = (a.pool - 1) / 2, K = a.K;
+  const float* raw = a.raw + g * a.m;
+  float* pooled = a.pooled + g * a.m;
   const uint32_t* pbits = reinterpret_cast<const uint32_t*>(pooled);
 
   for (int i = tid; i < 2048; i += NT) hist[i] = 0u;

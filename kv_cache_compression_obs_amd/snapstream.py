@@ -21,7 +21,8 @@ TORCH_DTYPE = {SS_F32: torch.float32, SS_BF16: torch.bfloat16}
 EXPORTS = ("ss_cache_slots", "ss_prefill_workspace_bytes", "ss_decode_workspace_bytes",
            "ss_decode_workspace_init", "ss_prefill_compress", "ss_decode_step",
            "ss_prefill_compress_timed", "ss_decode_step_timed", "ss_prefill_compress_lse",
-           "ss_prefill_compress_lse_timed", "ss_status_string")
+           "ss_prefill_compress_lse_timed", "ss_prefill_compress_varlen",
+           "ss_prefill_compress_varlen_timed", "ss_status_string")
 
 
 class ss_config(ctypes.Structure):
@@ -82,6 +83,12 @@ def lib() -> ctypes.CDLL:
         L.ss_prefill_compress_lse.restype = I32
         L.ss_prefill_compress_lse_timed.argtypes = L.ss_prefill_compress_lse.argtypes + [VP, VP]
         L.ss_prefill_compress_lse_timed.restype = I32
+        L.ss_prefill_compress_varlen.argtypes = [P(ss_config), VP, VP, VP, I32, VP, I32, VP, VP,
+                                                 P(ss_cache), VP, VP, VP, VP, SZ, VP]
+        L.ss_prefill_compress_varlen.restype = I32
+        L.ss_prefill_compress_varlen_timed.argtypes = (L.ss_prefill_compress_varlen.argtypes +
+                                                       [VP, VP])
+        L.ss_prefill_compress_varlen_timed.restype = I32
         L.ss_decode_workspace_init.argtypes = [P(ss_config), I32, VP, SZ, VP]
         L.ss_decode_workspace_init.restype = I32
         L.ss_status_string.argtypes = [I32]
@@ -210,6 +217,38 @@ def ss_prefill_compress(cfg: ss_config, q_obs, k, v, cache: Cache, rows=None, ra
         st = getattr(lib(), name + "_timed")(*args, events[0], events[1])
     if st != SS_OK:
         raise SnapStreamError(st, name)
+
+
+def ss_prefill_compress_varlen(cfg: ss_config, q_obs, k, v, cu_seqlens, max_L: int,
+                               cache: Cache, rows=None, lse=None, raw_out=None, pooled_out=None,
+                               sel_out=None, ws=None, stream=None, events=None) -> None:
+    """Build the fixed cache of b = q_obs.shape[0] requests of different
+    lengths: k [n_kv_heads, T, d_qk] and v packed per kv-head, request i =
+    tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (int32 device [b+1]); max_L bounds
+    every length.  lse: optional [b, n_q_heads, W] (one-pass scoring)."""
+    dt = TORCH_DTYPE[cfg.dtype]
+    for t, n in ((q_obs, "q_obs"), (k, "k"), (v, "v")):
+        _check(t, n, dt)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    _check(rows, "rows", torch.int32)
+    _check(lse, "lse", torch.float32)
+    for t, n in ((raw_out, "raw_out"), (pooled_out, "pooled_out")):
+        _check(t, n, torch.float32)
+    _check(sel_out, "sel_out", torch.int32)
+    b = int(q_obs.shape[0])
+    if ws is None:
+        ws = torch.empty(ss_prefill_workspace_bytes(cfg, b, max_L), dtype=torch.uint8,
+                         device=k.device)
+    cs = cache.struct()
+    args = (ctypes.byref(cfg), _ptr(q_obs), _ptr(k), _ptr(v), b, _ptr(cu_seqlens), int(max_L),
+            _ptr(lse), _ptr(rows), ctypes.byref(cs), _ptr(raw_out), _ptr(pooled_out),
+            _ptr(sel_out), _ptr(ws), ws.numel(), _stream(stream))
+    if events is None:
+        st = lib().ss_prefill_compress_varlen(*args)
+    else:
+        st = lib().ss_prefill_compress_varlen_timed(*args, events[0], events[1])
+    if st != SS_OK:
+        raise SnapStreamError(st, "ss_prefill_compress_varlen")
 
 
 def ss_decode_step(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, out, err_flag=None,
