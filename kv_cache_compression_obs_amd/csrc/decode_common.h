@@ -115,48 +115,64 @@ __device__ __forceinline__ void wave_sync() {
 // invalidate this XCD's whole L2 and slow every workgroup still streaming on
 // it.  The merge computes
 //   out[head, dv] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
-// in split order.  Each thread loads every split's (m, l, o) of its 4
-// outputs at once (batches of MB splits): one memory round trip per batch.
-template <typename T, int DV>
+// in split order.
+template <typename T, int DV, int NI>
 __device__ __forceinline__ void merge_splits(const DecodeArgs& a, size_t head0, int G, int ns,
                                              int tid, int nthreads) {
-  constexpr int MB = 16;
-  for (int idx = tid; idx < G * (DV / 4); idx += nthreads) {
-    const int g = idx / (DV / 4), d4 = idx % (DV / 4);
+  // Each thread merges NI outputs of one head (4 dims each, NO = DV/4/NI
+  // apart so that every load instruction stays coalesced; they share the
+  // splits' (m, l)) at once, MB splits per batch: one memory round trip per
+  // batch.  Loads are unconditional (a split index past ns rereads
+  // the last split), so no wait is forced between them; the surplus gets
+  // weight 0.
+  static_assert((DV / 4) % NI == 0, "an output group stays within one head");
+  constexpr int MB = NI > 1 ? 8 : 16;
+  constexpr int NO = DV / 4 / NI;
+  const int ngrp = G * NO;
+  for (int q = tid; q < ngrp; q += nthreads) {
+    const int g = q / NO, d40 = q % NO;
     const size_t base = (head0 + g) * a.n_split;
     const __amdgpu_buffer_rsrc_t ob = dev_buffer(a.part_o + base * DV, a.n_split * DV * 4);
     float M = -INFINITY, L = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int sb = 0; sb < ns; sb += MB) {
       float mv[MB], lv[MB];
-      f32x4_t ov[MB];
+      f32x4_t ov[MB][NI];
 #pragma unroll
       for (int j = 0; j < MB; ++j) {
-        const bool in = sb + j < ns;
-        const size_t s = base + sb + (in ? j : 0);
-        mv[j] = in ? ld_dev(a.part_ml + 2 * s) : -INFINITY;
-        lv[j] = in ? ld_dev(a.part_ml + 2 * s + 1) : 0.f;
-        ov[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (in) ov[j] = ld_dev4(ob, ((sb + j) * DV + 4 * d4) * 4);
+        const int sp = min(sb + j, ns - 1);
+        mv[j] = ld_dev(a.part_ml + 2 * (base + sp));
+        lv[j] = ld_dev(a.part_ml + 2 * (base + sp) + 1);
+#pragma unroll
+        for (int k = 0; k < NI; ++k) ov[j][k] = ld_dev4(ob, (sp * DV + 4 * (d40 + k * NO)) * 4);
       }
       float Mn = M;
 #pragma unroll
-      for (int j = 0; j < MB; ++j) Mn = fmaxf(Mn, mv[j]);
-      const float r = exp2f(M - Mn);
+      for (int j = 0; j < MB; ++j)
+        if (sb + j < ns) Mn = fmaxf(Mn, mv[j]);
+      // a batch of splits without slots leaves Mn at -inf: nothing to add
+      const float Mr = Mn == -INFINITY ? 0.f : Mn;
+      const float r = exp2f(M - Mr);
       L *= r;
-      acc *= r;
+#pragma unroll
+      for (int k = 0; k < NI; ++k) acc[k] *= r;
 #pragma unroll
       for (int j = 0; j < MB; ++j) {
-        const float w = exp2f(mv[j] - Mn);
+        const float w = sb + j < ns ? exp2f(mv[j] - Mr) : 0.f;
         L += w * lv[j];
-        acc += w * ov[j];
+#pragma unroll
+        for (int k = 0; k < NI; ++k) acc[k] += w * ov[j][k];
       }
       M = Mn;
     }
     const float inv = 1.f / L;
-    T* o = static_cast<T*>(a.out) + (head0 + g) * DV + 4 * d4;
+    T* o = static_cast<T*>(a.out) + (head0 + g) * DV + 4 * d40;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(acc[e] * inv);
+    for (int k = 0; k < NI; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[4 * k * NO + e] = from_f32<T>(acc[k][e] * inv);
   }
 }
 
