@@ -98,6 +98,10 @@ __device__ __forceinline__ bf16x8_t pack_bf16x8(const bf16_t* e) {
 }
 
 // ---------------------------------------------------------- cross-lane reduce
+// 2^x from the hardware instruction (v_exp_f32): no denormal results (they
+// flush to 0), -inf gives 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, WAVE));
 }

@@ -14,8 +14,10 @@
 //            chunks (score_rowstat_combine) into (max M, weight w = 1/sum);
 //   pass 2 (score_columns): over the middle keys only, recompute x and sum
 //            2^(x - M) * w over the rows of the group, per key.
-// Both passes compute x with the same instruction sequence, so pass 2 sees
-// bit-identical logits to the ones pass 1 normalised.
+// Both passes form x - M with the same fma (x = scale*log2(e) * q.k), so pass 2
+// sees the logits pass 1 normalised.  Exponentials use the hardware exp2
+// (fast_exp2): results below 2^-126 of a row's maximum flush to zero, a
+// negligible share of a sum whose largest term is 1.
 #include "common.h"
 #include "launch.h"
 
@@ -107,12 +109,17 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
   const int k0 = chunk * a.chunk1, k1 = min(k0 + a.chunk1, pr.L);
   const T* kbase = static_cast<const T*>(a.k) + pr.row0 * D;
 
-  float m[4], s[4];
+  // Per lane and row: running max of the raw dot products (ma), the same in
+  // log2 units (m = ma * scale_log2) and the sum of 2^(x - m).
+  float ma[4], m[4], s[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
+    ma[r] = m[r] = -INFINITY;
     s[r] = 0.f;
   }
+  const float sc = a.scale_log2;
+  // keys of a tile wholly below this bound are visible to every row and real
+  const int open_end = min(k1, pr.L - a.W + 1);
   u32x4_t ld[KTile::NLD];
   KTile::load(ld, kbase, k0, k1, tid);
   KTile::store(lds, ld, tid);
@@ -123,30 +130,38 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
     const bool more = t0 + KT < k1;
     if (more) KTile::load(ld, kbase, t0 + KT, k1, tid);
     if (active) {
-      float x[NKB][4];
+      f32x4_t acc[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        acc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc = MM::mma(qf[c], KTile::bfrag(cur, kb, c, col, qg), acc);
-        const int key = t0 + 16 * kb + col;
+        for (int c = 0; c < NC; ++c)
+          acc[kb] = MM::mma(qf[c], KTile::bfrag(cur, kb, c, col, qg), acc[kb]);
+      }
+      if (t0 + KT > open_end) {  // (uniform) the ragged end or the causal window
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[kb][r] = (key < k1 && key <= lim[r]) ? acc[r] * a.scale_log2 : -INFINITY;
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int key = t0 + 16 * kb + col;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!(key < k1 && key <= lim[r])) acc[kb][r] = -INFINITY;
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float tm = x[0][r];
+        float tm = acc[0][r];
 #pragma unroll
-        for (int kb = 1; kb < NKB; ++kb) tm = fmaxf(tm, x[kb][r]);
-        const float mn = fmaxf(m[r], tm);
-        if (mn != -INFINITY) {
-          float add = 0.f;
+        for (int kb = 1; kb < NKB; ++kb) tm = fmaxf(tm, acc[kb][r]);
+        const float mn = fmaxf(ma[r], tm);
+        // x - m = fma(acc, sc, -m); a row with no visible key yet keeps
+        // (m, s) = (-inf, 0): its exponents are -inf (with m taken as 0)
+        const float mx = mn == -INFINITY ? 0.f : mn * sc;
+        float add = 0.f;
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) add += exp2f(x[kb][r] - mn);
-          s[r] = s[r] * exp2f(m[r] - mn) + add;
-          m[r] = mn;
-        }
+        for (int kb = 0; kb < NKB; ++kb) add += fast_exp2(__builtin_fmaf(acc[kb][r], sc, -mx));
+        s[r] = s[r] * fast_exp2(m[r] - mx) + add;
+        ma[r] = mn;
+        m[r] = mn == -INFINITY ? -INFINITY : mx;
       }
     }
     if (more) KTile::store(lds + ((t + 1) & 1) * KTile::BYTES, ld, tid);
@@ -160,7 +175,7 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
     M = xor_max(M, 2);
     M = xor_max(M, 4);
     M = xor_max(M, 8);
-    float sv = m[r] == -INFINITY ? 0.f : s[r] * exp2f(m[r] - M);
+    float sv = m[r] == -INFINITY ? 0.f : s[r] * fast_exp2(m[r] - M);
     sv = xor_sum(sv, 1);
     sv = xor_sum(sv, 2);
     sv = xor_sum(sv, 4);
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
         float cs = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          cs += ok[r] ? exp2f(acc[r] * a.scale_log2 - M[r]) * w[r] : 0.f;
+          cs += ok[r] ? fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -M[r])) * w[r] : 0.f;
         cs = xor_sum(cs, 16);
         cs = xor_sum(cs, 32);
         if (qg == 0) red[t & 1][wave][16 * kb + col] = cs;
