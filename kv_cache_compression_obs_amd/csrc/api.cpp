@@ -74,9 +74,9 @@ PrefillPlan plan_prefill(const ss_config* c, int b, int L) {
   const int G = c->n_q_heads / c->n_kv_heads;
   p.m = L - c->L_sink - c->L_recent;
   p.Rg = (G * c->W + 15) / 16 * 16;
-  p.chunk1 = 2048;
+  p.chunk1 = ss::SCORE_CHUNK1;
   p.n_chunk1 = (L + p.chunk1 - 1) / p.chunk1;
-  p.chunk2 = 1024;
+  p.chunk2 = ss::SCORE_CHUNK2;
   p.n_chunk2 = (p.m + p.chunk2 - 1) / p.chunk2;
   const size_t groups = static_cast<size_t>(b) * c->n_kv_heads;
   size_t off = 0;

@@ -112,5 +112,14 @@ constexpr int DECODE_MAX_TILES = SS_DECODE_MAX_TILES;
 // banks).
 constexpr int decode_vrow_stride(int row_bytes) { return row_bytes + 32; }
 constexpr int SCORE_KT_MAX = 64;  // keys per score tile (chunks are multiples of it)
+// Keys per workgroup of the two score passes (multiples of SCORE_KT_MAX).
+#ifndef SS_SCORE_CHUNK1
+#define SS_SCORE_CHUNK1 2048
+#endif
+#ifndef SS_SCORE_CHUNK2
+#define SS_SCORE_CHUNK2 1024
+#endif
+constexpr int SCORE_CHUNK1 = SS_SCORE_CHUNK1;
+constexpr int SCORE_CHUNK2 = SS_SCORE_CHUNK2;
 
 }  // namespace ss
