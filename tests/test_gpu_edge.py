@@ -1,0 +1,45 @@
+"""GPU parity on the degenerate and boundary configurations of the method:
+no middle budget (K = 0), no sinks (L_sink = 0), no pooling (pool = 1), a
+one-query observation window (W = 1), plain multi-head attention (G = 1), the
+largest group the score kernels take (G = 16, G*W = 256 rows), and rotary
+embedding over part of the head (decode rotates dims 32..95 of 128) or over
+every dim of an fp32 head.  Each configuration runs the prefill comparison
+(scores, selection, slot map, gathered rows) and a decode run across the ring
+wrap (outputs, written rows, n_tokens) against the oracle."""
+import pytest
+
+from kv_cache_compression_obs_amd import synth
+from parity import decode_case, prefill_case, say
+
+pytestmark = pytest.mark.gpu
+
+TINY = "tiny_fp32"          # 4q/2kv, d64, fp32, S/K/R = 4/64/128, W 16, pool 7
+SMALL = "llama8b_c4k"       # 32q/8kv, d128, bf16, rope 5e5
+
+CASES = {
+    "no_middle_budget": (TINY, dict(K=0), 512),
+    "no_sinks": (TINY, dict(L_sink=0), 512),
+    "no_pooling": (TINY, dict(pool=1), 512),
+    "one_query_window": (TINY, dict(W=1), 512),
+    "multi_head_G1": (TINY, dict(n_q_heads=2, n_kv_heads=2), 512),
+    "fp32_full_rope": (TINY, dict(rope_theta=1e4, rope_begin=0, rope_end=64), 512),
+    "largest_group_G16": (SMALL, dict(B=2, n_q_heads=32, n_kv_heads=2, W=16, L_sink=16, K=200,
+                                      L_recent=512), 3000),
+    "partial_rope": (SMALL, dict(B=2, rope_begin=32, rope_end=96, L_sink=16, K=200,
+                                 L_recent=512), 3000),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_edge_prefill(case):
+    name, kw, L = CASES[case]
+    prefill_case(synth.workload(name, **kw), 61, L=L)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_edge_decode(case):
+    name, kw, L = CASES[case]
+    w = synth.workload(name, **kw)
+    steps = w["L_recent"] + 40  # every ring slot rewritten at least once
+    say(f"decode edge {case} C={w['C']} L={L} steps={steps}")
+    decode_case(w, L=L, steps=steps, seed=62, check_every=max(1, steps // 25))
