@@ -286,6 +286,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-uncompressed", action="store_true",
                     help="skip the uncompressed-cache baseline (decode over C = L slots)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the step only: skip the given-lse prefill, the varlen admission "
+                         "and the uncompressed baseline (for profiling runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (a kernel of "
                          "known traffic, to calibrate FETCH_SIZE/WRITE_SIZE counters)")
@@ -423,9 +426,10 @@ def main():
             "frac_bf16_peak_executed": round(fl_exec / score_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         },
     }
-    res["given_lse"] = given_lse_prefill(ss, torch, w, cfg, inp)
-    res["varlen_admission"] = varlen_admission(ss, torch, synth, w, cfg)
-    if not args.no_uncompressed:
+    if not args.no_extras:
+        res["given_lse"] = given_lse_prefill(ss, torch, w, cfg, inp)
+        res["varlen_admission"] = varlen_admission(ss, torch, synth, w, cfg)
+    if not (args.no_uncompressed or args.no_extras):
         caches.clear()                      # frees the compressed copies
         res["uncompressed_baseline"] = uncompressed_baseline(
             ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_avg_s)
