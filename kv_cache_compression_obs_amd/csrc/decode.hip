@@ -41,7 +41,7 @@ constexpr int DW = DECODE_WAVES;  // waves per decode workgroup
 // shared by all XCDs; the last workgroup of the (row, kv-head) to take a
 // ticket (device-scope counter) merges every split in split order and resets
 // the counter.
-template <typename T, int D, int DV, bool ALIAS>
+template <typename T, int D, int DV>
 __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   using MM = Mma<T>;
   using frag = typename MM::frag;
@@ -50,7 +50,6 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   constexpr int NDB = DV / 16;
   constexpr int TS = DECODE_TILE;
   constexpr int VROW = DV * static_cast<int>(sizeof(T));
-  constexpr int VSTRIDE = ALIAS ? D : DV;
   constexpr int LROW = decode_vrow_stride(VROW);
   constexpr int VCH = VROW / 16;
   constexpr int VLD = TS * VCH / 64;
@@ -78,7 +77,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(h) * G;
   const int col = lane & 15, qg = lane >> 4;
   const T* kb = static_cast<const T*>(a.kc) + gh * a.C * D;
-  const T* vb = ALIAS ? kb : static_cast<const T*>(a.vc) + gh * a.C * DV;
+  const T* vb = static_cast<const T*>(a.vc) + gh * a.C * DV;
   const int koff = 4 * (col & 3) + (col >> 2);
   frag kf[2][NC];
   u32x4_t vr[VLD];
@@ -97,7 +96,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
       const int id = i * 64 + lane;
       const int s = min(t0 + id / VCH, hi - 1);
       vr[i] = *reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const char*>(vb + static_cast<size_t>(s) * VSTRIDE) + (id % VCH) * 16);
+          reinterpret_cast<const char*>(vb + static_cast<size_t>(s) * DV) + (id % VCH) * 16);
     }
   };
   // ---------------------------------------------------------------- loads
@@ -126,7 +125,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
     if (off < qbytes) qld[j] = *reinterpret_cast<const u32x4_t*>(qsrc + off);
   }
   if (tid * 16 < KROW) kld = *reinterpret_cast<const u32x4_t*>(ksrc + tid * 16);
-  if (!ALIAS && tid * 16 < VROW)
+  if (tid * 16 < VROW)
     vld = *reinterpret_cast<const u32x4_t*>(
         reinterpret_cast<const char*>(static_cast<const T*>(a.v_new) + gh * DV) + tid * 16);
 
@@ -161,7 +160,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
     if (off < qbytes) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(qraw) + off) = qld[j];
   }
   if (tid * 16 < KROW) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(kraw) + tid * 16) = kld;
-  if (!ALIAS && tid * 16 < VROW) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(vnew) + tid * 16) = vld;
+  if (tid * 16 < VROW) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(vnew) + tid * 16) = vld;
   for (int i = tid; i < half; i += NT) {
     const double ang = static_cast<double>(p) * a.inv_freq[i];
     double sv, cv;
@@ -182,7 +181,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
       knew[d] = kv;
       kdst[d] = kv;
     }
-    if (!ALIAS && tid * 16 < VROW)
+    if (tid * 16 < VROW)
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(static_cast<T*>(a.vc) +
                                                           (gh * a.C + slot) * DV) + tid * 16) = vld;
     if (tid == 0) {
@@ -194,8 +193,6 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  if (ALIAS && own)  // the value is the first DV dims of the new latent row
-    for (int d = tid; d < DV; d += 64 * DW) vnew[d] = knew[d];
 
   frag qf[NP][NC];
 #pragma unroll
@@ -348,10 +345,10 @@ __global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* c, int n) {
   if (i < n) c[i] = 0;
 }
 
-template <typename T, int D, int DV, bool ALIAS>
+template <typename T, int D, int DV>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
-  decode_kernel<T, D, DV, ALIAS><<<dim3(a.n_split, a.Hkv, a.B), 64 * DW, 0, st>>>(a);
+  decode_kernel<T, D, DV><<<dim3(a.n_split, a.Hkv, a.B), 64 * DW, 0, st>>>(a);
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -361,12 +358,12 @@ hipError_t run_decode(const DecodeArgs& a, hipStream_t st, hipEvent_t ev0, hipEv
 hipError_t launch_decode(int dtype, int D, int DV, int alias, const DecodeArgs& a,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (alias) return launch_decode_mla(dtype, D, DV, a, st, ev0, ev1);
-  if (dtype == 0 && D == 64 && DV == 64) return run_decode<float, 64, 64, false>(a, st, ev0, ev1);
+  if (dtype == 0 && D == 64 && DV == 64) return run_decode<float, 64, 64>(a, st, ev0, ev1);
   if (dtype == 0 && D == 128 && DV == 128)
-    return run_decode<float, 128, 128, false>(a, st, ev0, ev1);
-  if (dtype == 1 && D == 64 && DV == 64) return run_decode<bf16_t, 64, 64, false>(a, st, ev0, ev1);
+    return run_decode<float, 128, 128>(a, st, ev0, ev1);
+  if (dtype == 1 && D == 64 && DV == 64) return run_decode<bf16_t, 64, 64>(a, st, ev0, ev1);
   if (dtype == 1 && D == 128 && DV == 128)
-    return run_decode<bf16_t, 128, 128, false>(a, st, ev0, ev1);
+    return run_decode<bf16_t, 128, 128>(a, st, ev0, ev1);
   return hipErrorInvalidValue;
 }
 
