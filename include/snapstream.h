@@ -106,7 +106,9 @@ int32_t ss_cache_slots(const ss_config* cfg);
 
 /* Workspace (device bytes) needed by ss_prefill_compress for b requests of
  * L prompt tokens, and by ss_decode_step for a cache of B_max rows.  0 if the
- * arguments are invalid. */
+ * arguments are invalid.  The prefill size depends on the current device (the
+ * score passes split the keys to fill whole rounds of its compute units):
+ * query it with the device current that the prefill call will run on. */
 size_t ss_prefill_workspace_bytes(const ss_config* cfg, int32_t b, int32_t L);
 size_t ss_decode_workspace_bytes(const ss_config* cfg, int32_t B_max);
 

@@ -74,11 +74,20 @@ PrefillPlan plan_prefill(const ss_config* c, int b, int L) {
   const int G = c->n_q_heads / c->n_kv_heads;
   p.m = L - c->L_sink - c->L_recent;
   p.Rg = (G * c->W + 15) / 16 * 16;
-  p.chunk1 = ss::SCORE_CHUNK1;
-  p.n_chunk1 = (L + p.chunk1 - 1) / p.chunk1;
-  p.chunk2 = ss::SCORE_CHUNK2;
-  p.n_chunk2 = (p.m + p.chunk2 - 1) / p.chunk2;
   const size_t groups = static_cast<size_t>(b) * c->n_kv_heads;
+  // chunk lengths that fill whole rounds of the current device; the
+  // compile-time defaults when it cannot be queried
+  int slots1 = 0, slots2 = 0;
+  if (ss::prefill_score_slots(c->dtype, c->d_qk, p.Rg, &slots1, &slots2) == hipSuccess) {
+    p.chunk1 = ss::score_chunk(L, static_cast<long long>(groups), slots1);
+    p.chunk2 = ss::score_chunk(p.m, static_cast<long long>(groups), slots2);
+  } else {
+    (void)hipGetLastError();  // a failed query leaves no error for later calls
+    p.chunk1 = ss::SCORE_CHUNK1;
+    p.chunk2 = ss::SCORE_CHUNK2;
+  }
+  p.n_chunk1 = (L + p.chunk1 - 1) / p.chunk1;
+  p.n_chunk2 = (p.m + p.chunk2 - 1) / p.chunk2;
   size_t off = 0;
   p.off_part1 = off;
   off += align_up(groups * p.Rg * p.n_chunk1 * 2 * sizeof(float));

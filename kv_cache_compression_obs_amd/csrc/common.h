@@ -109,6 +109,21 @@ __device__ __forceinline__ float xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, WAVE);
 }
 
+// v + the value of lane l ^ 16 (resp. l ^ 32), through the gfx950 row-swap
+// instructions (no LDS): v_permlane16_swap exchanges the odd 16-lane rows of
+// its first operand with the even rows of its second, so with both operands v
+// the two results hold, in every lane, v and the partner's v.
+__device__ __forceinline__ float sum_across_16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_across_32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace ss

@@ -112,7 +112,9 @@ constexpr int DECODE_MAX_TILES = SS_DECODE_MAX_TILES;
 // banks).
 constexpr int decode_vrow_stride(int row_bytes) { return row_bytes + 32; }
 constexpr int SCORE_KT_MAX = 64;  // keys per score tile (chunks are multiples of it)
-// Keys per workgroup of the two score passes (multiples of SCORE_KT_MAX).
+// Keys per workgroup of the two score passes when the device cannot be
+// queried (multiples of SCORE_KT_MAX); otherwise the host sizes the chunks so
+// that the workgroups fill whole rounds of the device (see score_chunk).
 #ifndef SS_SCORE_CHUNK1
 #define SS_SCORE_CHUNK1 2048
 #endif
@@ -121,5 +123,48 @@ constexpr int SCORE_KT_MAX = 64;  // keys per score tile (chunks are multiples o
 #endif
 constexpr int SCORE_CHUNK1 = SS_SCORE_CHUNK1;
 constexpr int SCORE_CHUNK2 = SS_SCORE_CHUNK2;
+// Fixed cost of one score workgroup (start, queries, final reduction) in
+// keys, for the chunk choice.
+constexpr int SCORE_WG_OVERHEAD_KEYS = 128;
+// Key tiles in flight per score workgroup (ring slots in LDS), capped by an
+// LDS budget per workgroup.
+#ifndef SS_SCORE_NBUF
+#define SS_SCORE_NBUF 2
+#endif
+constexpr int SCORE_NBUF = SS_SCORE_NBUF;
+// Score key tiles in LDS: 1 = XOR-permuted bf16 rows of 128 or 256 bytes,
+// 0 = rows padded by 16 bytes (affine fragment addresses).
+#ifndef SS_SCORE_SWIZZLE
+#define SS_SCORE_SWIZZLE 1
+#endif
+constexpr bool SCORE_SWIZZLE = SS_SCORE_SWIZZLE != 0;
+constexpr int SCORE_LDS_BUDGET = 156 * 1024;
+
+// Workgroups of score pass 1 / pass 2 that run at once on the current
+// device (compute units x resident workgroups per unit) for this dtype, head
+// size and padded group row count; hipErrorInvalidValue for a shape without
+// kernels, or the HIP error of the device query.
+hipError_t prefill_score_slots(int dtype, int D, int Rg, int* slots1, int* slots2);
+
+// Keys per workgroup for `keys` keys in each of `groups` groups when `slots`
+// workgroups run at once: the multiple of SCORE_KT_MAX that minimises
+// rounds x (chunk + SCORE_WG_OVERHEAD_KEYS).
+inline int score_chunk(int keys, long long groups, int slots) {
+  const int tiles = (keys + SCORE_KT_MAX - 1) / SCORE_KT_MAX;
+  int best = tiles * SCORE_KT_MAX;
+  long long best_cost = -1;
+  for (int n = 1; n <= tiles; ++n) {
+    const int ct = (tiles + n - 1) / n;  // tiles per chunk
+    const int n_eff = (tiles + ct - 1) / ct;
+    const long long rounds = (groups * n_eff + slots - 1) / slots;
+    const long long cost =
+        rounds * (static_cast<long long>(ct) * SCORE_KT_MAX + SCORE_WG_OVERHEAD_KEYS);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = ct * SCORE_KT_MAX;
+    }
+  }
+  return best;
+}
 
 }  // namespace ss

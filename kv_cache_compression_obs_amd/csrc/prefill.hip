@@ -25,43 +25,117 @@ namespace ss {
 
 namespace {
 
-// A key tile of KT rows staged in LDS by the NT threads of a score workgroup.
-template <typename T, int D, int KT, int NT>
-struct KeyTile {
-  static constexpr int ES = static_cast<int>(sizeof(T));
-  static constexpr int KROW = D * ES;      // bytes of one key row
-  static constexpr int LROW = KROW + 16;   // LDS row stride (bytes)
-  static constexpr int KCH = KROW / 16;    // 16-byte chunks per row
-  static constexpr int NLD = cdiv(KT * KCH, NT);
-  static constexpr int BYTES = KT * LROW;
+// A ring of NBUF key tiles (KT rows each) in LDS, filled by direct
+// global->LDS loads: lane l of one load writes bytes [16 l, 16 l + 16) of a
+// 1 KB LDS block, so a tile takes NI such loads and no registers.
+//
+// Layout in 16-byte units (KCH units per key row):
+//  - bf16 rows of 8 or 16 units: unit u = row * KCH + j is stored at
+//    u ^ (u / 16 mod 16), a permutation inside each 256-byte group.  The 16
+//    lanes that read one B fragment (16 consecutive rows, the same unit of
+//    each) land on 16 different groups of 4 banks, and the fragment address
+//    is a per-lane term plus a constant per 16-row block;
+//  - any other row (fp32, whose fragments are single dwords, or a row size
+//    that is not a power of two): rows padded to KCH + 1 units, so fragment
+//    addresses stay affine (immediate offsets); the pad unit gets a copy of
+//    the row's last unit.
+// Loads i = w, w + NWV, ... of a tile belong to wave w, which counts them on
+// its own vmcnt: after waiting for its loads of tile t and meeting the
+// workgroup barrier, every wave sees the whole of tile t.
+typedef const __attribute__((address_space(1))) void* global_ptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-  // rows t0 .. t0+KT-1 of kbase (clamped to kend-1) into registers
-  static __device__ __forceinline__ void load(u32x4_t (&r)[NLD], const T* kbase, int t0, int kend,
-                                              int tid) {
+template <typename T, int D, int KT, int NWV, int NBUF>
+struct KeyRing {
+  static constexpr int ES = static_cast<int>(sizeof(T));
+  static constexpr int KCH = D * ES / 16;  // 16-byte units per key row
+  static constexpr bool SWZ = SCORE_SWIZZLE && ES == 2 && (KCH == 8 || KCH == 16);
+  static constexpr int RU = SWZ ? KCH : KCH + 1;  // units per row in LDS
+  static constexpr int NI = cdiv(KT * RU, 64);   // 1 KB loads per tile
+  static constexpr int BYTES = NI * 1024;        // one ring slot
+  static constexpr int LO = NI / NWV;            // loads per wave and tile (LO + 1
+  static constexpr int HI_WAVES = NI % NWV;      // for the first HI_WAVES waves)
+  static_assert(NBUF >= 2 && (NBUF - 2) * (LO + 1) <= 63, "vmcnt range");
+  static_assert(D * ES % 16 == 0, "key rows are whole 16-byte units");
+
+  static __device__ __forceinline__ int perm(int u) { return u ^ ((u >> 4) & 15); }
+  static __device__ __forceinline__ int unit(int row, int j) {
+    if constexpr (SWZ) return perm(row * KCH + j);
+    else return row * RU + j;
+  }
+
+  // keys t0 .. t0+KT-1 of kbase (rows clamped to kend-1) into ring slot `slot`
+  static __device__ __forceinline__ void issue(char* slot, const T* kbase, int t0, int kend,
+                                               int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int id = i * NT + tid;
-      if (id < KT * KCH) {
-        const int key = min(t0 + id / KCH, kend - 1);
-        r[i] = *reinterpret_cast<const u32x4_t*>(
-            reinterpret_cast<const char*>(kbase + static_cast<size_t>(key) * D) + (id % KCH) * 16);
+    for (int k = 0; k <= LO; ++k) {
+      const int i = wave + k * NWV;
+      if (k < LO || i < NI) {  // wave-uniform
+        const int p = i * 64 + lane;
+        int row, j;
+        if constexpr (SWZ) {
+          const int u = perm(p);
+          row = u / KCH;
+          j = u % KCH;
+        } else {
+          row = p / RU;
+          j = min(p % RU, KCH - 1);
+        }
+        const int key = min(t0 + row, kend - 1);
+        const char* src =
+            reinterpret_cast<const char*>(kbase + static_cast<size_t>(key) * D) + j * 16;
+        __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(slot + i * 1024), 16, 0, 0);
       }
     }
   }
-  static __device__ __forceinline__ void store(char* buf, const u32x4_t (&r)[NLD], int tid) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int id = i * NT + tid;
-      if (id < KT * KCH)
-        *reinterpret_cast<u32x4_t*>(buf + (id / KCH) * LROW + (id % KCH) * 16) = r[i];
-    }
+
+  // Called once the first NBUF - 1 tiles are issued: wait for every load of
+  // this wave, those tiles and the loads before them (queries, row
+  // statistics).  The compiler sees this wait, so it keeps no wait for those
+  // loads inside the loop (where it cannot count the tile loads in flight).
+  static __device__ __forceinline__ void wait_all() {
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
   }
+
+  // Wait until this wave's loads of the oldest tile in flight have landed
+  // (NBUF - 2 newer tiles may still be loading), then the workgroup barrier.
+  // lgkmcnt(0): this wave's LDS reads and writes are done as well.
+  static __device__ __forceinline__ void wait_barrier(int wave) {
+    if (wave < HI_WAVES)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NBUF - 2) * (LO + 1)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NBUF - 2) * LO) : "memory");
+    asm volatile("s_barrier" ::: "memory");
+  }
+  // no load may still write LDS when the workgroup ends
+  static __device__ __forceinline__ void drain() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
   // B operand (K^T) fragment: lane (col, qg) takes key 16*kb + col, dims
-  // c*KSTEP + qg*KPL ..
-  static __device__ __forceinline__ typename Mma<T>::frag bfrag(const char* buf, int kb, int c,
-                                                                int col, int qg) {
-    return Mma<T>::load(reinterpret_cast<const T*>(
-        buf + (16 * kb + col) * LROW + (c * Mma<T>::KSTEP + qg * Mma<T>::KPL) * ES));
+  // c*KSTEP + qg*KPL ..  Its byte address in a slot is a constant per (kb, c)
+  // plus a lane term that repeats every KBP blocks of 16 rows and, padded,
+  // is the same for every c: NL = KBP * NCL lane terms in registers.
+  static constexpr int NCB = D / Mma<T>::KSTEP;              // fragments per row
+  static constexpr int KBP = SWZ ? 16 / KCH : 1;
+  static constexpr int NCL = SWZ ? NCB : 1;
+  static constexpr int BLOCK = KBP * 16 * RU * 16;          // bytes of KBP blocks of 16 rows
+  static __device__ __forceinline__ int frag_byte(int row, int c, int qg) {
+    const int byte = (c * Mma<T>::KSTEP + qg * Mma<T>::KPL) * ES;
+    return unit(row, byte >> 4) * 16 + (byte & 15);
+  }
+  static __device__ __forceinline__ void lane_terms(int (&lt)[KBP][NCL], int col, int qg) {
+#pragma unroll
+    for (int p = 0; p < KBP; ++p)
+#pragma unroll
+      for (int c = 0; c < NCL; ++c) lt[p][c] = frag_byte(16 * p + col, c, qg);
+  }
+  static __device__ __forceinline__ typename Mma<T>::frag bfrag(const char* slot,
+                                                                const int (&lt)[KBP][NCL], int kb,
+                                                                int c) {
+    const int off = SWZ ? (kb / KBP) * BLOCK + lt[kb % KBP][c]
+                        : kb * BLOCK + c * Mma<T>::KSTEP * ES + lt[0][0];
+    return Mma<T>::load(reinterpret_cast<const T*>(slot + off));
   }
 };
 
@@ -81,17 +155,23 @@ __device__ __forceinline__ void load_q(typename Mma<T>::frag (&qf)[D / Mma<T>::K
 
 // Pass 1.  Grid (n_chunk1, Hkv, b), NWV waves.  Wave w owns rows 16w .. 16w+15
 // of the group; accumulator lane (col, qg) register r holds row 16w + 4qg + r
-// and key 16kb + col of the tile.  Each lane keeps running (max, sum) of its
-// rows over the keys it sees; the 16 lanes of a row are merged at the end.
-template <typename T, int D, int KT, int NWV>
+// and key 16kb + col of the tile.  Each lane keeps, per row, a reference
+// maximum m (log2 units) and the sum of 2^(x - m) over the keys it sees; the
+// 16 lanes of a row are merged at the end.  m is raised only when a tile's
+// maximum exceeds it by more than 2^LAZY, so the terms stay below 2^LAZY and
+// the rescale (one exp2 per row) is skipped by the whole wave on most tiles.
+template <typename T, int D, int KT, int NWV, int NBUF>
 __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) {
   using MM = Mma<T>;
-  using KTile = KeyTile<T, D, KT, 64 * NWV>;
+  using Ring = KeyRing<T, D, KT, NWV, NBUF>;
   constexpr int NC = D / MM::KSTEP;
   constexpr int NKB = KT / 16;
-  __shared__ __attribute__((aligned(16))) char lds[2 * KTile::BYTES];
+  constexpr float LAZY = 8.f;
+  constexpr float EMPTY = -0x1p126f;  // m of a row that has seen no key yet (finite: no inf - inf)
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * Ring::BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, qg = lane >> 4;
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const bool active = 16 * wave < a.G * a.W;  // wave-uniform
@@ -100,73 +180,88 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
 
   typename MM::frag qf[NC];
   load_q<T, D>(qf, a, bi, h, 16 * wave + col, qg);
-  int lim[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 16 * wave + 4 * qg + r;
-    lim[r] = row < a.G * a.W ? pr.L - a.W + row % a.W : -1;  // last visible key
-  }
+  int lt[Ring::KBP][Ring::NCL];
+  Ring::lane_terms(lt, col, qg);
   const int k0 = chunk * a.chunk1, k1 = min(k0 + a.chunk1, pr.L);
   const T* kbase = static_cast<const T*>(a.k) + pr.row0 * D;
 
-  // Per lane and row: running max of the raw dot products (ma), the same in
-  // log2 units (m = ma * scale_log2) and the sum of 2^(x - m).
-  float ma[4], m[4], s[4];
+  const float sc = a.scale_log2;
+  const float lazy_raw = LAZY / sc;  // LAZY in raw dot-product units
+  float m[4], s[4], thr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    ma[r] = m[r] = -INFINITY;
+    m[r] = EMPTY;
     s[r] = 0.f;
+    thr[r] = -INFINITY;  // the first visible key raises m
   }
-  const float sc = a.scale_log2;
   // keys of a tile wholly below this bound are visible to every row and real
   const int open_end = min(k1, pr.L - a.W + 1);
-  u32x4_t ld[KTile::NLD];
-  KTile::load(ld, kbase, k0, k1, tid);
-  KTile::store(lds, ld, tid);
-  __syncthreads();
-  int t = 0;
-  for (int t0 = k0; t0 < k1; t0 += KT, ++t) {
-    const char* cur = lds + (t & 1) * KTile::BYTES;
-    const bool more = t0 + KT < k1;
-    if (more) KTile::load(ld, kbase, t0 + KT, k1, tid);
-    if (active) {
+  // the first NBUF - 1 tiles in flight; each step then refills the slot its
+  // predecessor used (tiles past the chunk read its last key)
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    Ring::issue(lds + i * Ring::BYTES, kbase, k0 + i * KT, k1, wave, lane);
+  Ring::wait_all();
+  for (int base = k0; base < k1; base += NBUF * KT) {
+#pragma unroll
+    for (int sl = 0; sl < NBUF; ++sl) {  // tile at t0 sits in slot sl (a constant here)
+      const int t0 = base + sl * KT;
+      if (t0 >= k1) break;
+      Ring::wait_barrier(wave);  // tile t0 in LDS; every wave is done with the previous one
+      Ring::issue(lds + ((sl + NBUF - 1) % NBUF) * Ring::BYTES, kbase, t0 + (NBUF - 1) * KT, k1,
+                  wave, lane);
+      if (!active) continue;
+      const char* cur = lds + sl * Ring::BYTES;
       f32x4_t acc[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         acc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          acc[kb] = MM::mma(qf[c], KTile::bfrag(cur, kb, c, col, qg), acc[kb]);
+          acc[kb] = MM::mma(qf[c], Ring::bfrag(cur, lt, kb, c), acc[kb]);
       }
       if (t0 + KT > open_end) {  // (uniform) the ragged end or the causal window
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int key = t0 + 16 * kb + col;
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * wave + 4 * qg + r;
+          const int lim = row < a.G * a.W ? pr.L - a.W + row % a.W : -1;  // last visible key
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (!(key < k1 && key <= lim[r])) acc[kb][r] = -INFINITY;
+          for (int kb = 0; kb < NKB; ++kb) {
+            const int key = t0 + 16 * kb + col;
+            if (!(key < k1 && key <= lim)) acc[kb][r] = -INFINITY;
+          }
         }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      // raise m when the tile's largest raw dot product passes thr, the
+      // raw-units image of m + LAZY
+      auto tile_max = [&](int r) {
         float tm = acc[0][r];
 #pragma unroll
         for (int kb = 1; kb < NKB; ++kb) tm = fmaxf(tm, acc[kb][r]);
-        const float mn = fmaxf(ma[r], tm);
-        // x - m = fma(acc, sc, -m); a row with no visible key yet keeps
-        // (m, s) = (-inf, 0): its exponents are -inf (with m taken as 0)
-        const float mx = mn == -INFINITY ? 0.f : mn * sc;
-        float add = 0.f;
+        return tm;
+      };
+      bool raise = false;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) add += fast_exp2(__builtin_fmaf(acc[kb][r], sc, -mx));
-        s[r] = s[r] * fast_exp2(m[r] - mx) + add;
-        ma[r] = mn;
-        m[r] = mn == -INFINITY ? -INFINITY : mx;
+      for (int r = 0; r < 4; ++r) raise |= tile_max(r) > thr[r];
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform; rare once m settles
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float tm = tile_max(r);
+          if (tm > thr[r]) {
+            const float mn = tm * sc;
+            s[r] *= fast_exp2(m[r] - mn);
+            m[r] = mn;
+            thr[r] = tm + lazy_raw;
+          }
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[r] += fast_exp2(__builtin_fmaf(acc[kb][r], sc, -m[r]));
     }
-    if (more) KTile::store(lds + ((t + 1) & 1) * KTile::BYTES, ld, tid);
-    __syncthreads();
   }
+  Ring::drain();
   if (!active) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -175,7 +270,7 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
     M = xor_max(M, 2);
     M = xor_max(M, 4);
     M = xor_max(M, 8);
-    float sv = m[r] == -INFINITY ? 0.f : s[r] * fast_exp2(m[r] - M);
+    float sv = s[r] * fast_exp2(m[r] - M);
     sv = xor_sum(sv, 1);
     sv = xor_sum(sv, 2);
     sv = xor_sum(sv, 4);
@@ -183,7 +278,7 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
     const int row = 16 * wave + 4 * qg + r;
     if (col == 0 && row < a.Rg) {
       const size_t idx = ((static_cast<size_t>(bi) * a.Hkv + h) * a.Rg + row) * a.n_chunk1 + chunk;
-      a.part1[2 * idx] = M;
+      a.part1[2 * idx] = M == EMPTY ? -INFINITY : M;
       a.part1[2 * idx + 1] = sv;
     }
   }
@@ -235,17 +330,23 @@ __global__ __launch_bounds__(256) void lse_rowstat_kernel(PrefillArgs a) {
 // Pass 2.  Grid (n_chunk2, Hkv, b) over the middle keys [S, L-R).  Every
 // middle key is visible to every observation row (the window lies inside the
 // recent region), so no causal mask.  Column sums: 4 rows in registers, then
-// the 4 lane groups (xor 16, 32), then the NWV waves through LDS in wave order.
-template <typename T, int D, int KT, int NWV>
+// the 4 lane groups (lane swaps across 16 and 32), then the NWV waves through
+// LDS in wave order.  Rows past G*W have zero queries and weight 0, so they
+// add exact zeros.
+template <typename T, int D, int KT, int NWV, int NBUF>
 __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) {
   using MM = Mma<T>;
-  using KTile = KeyTile<T, D, KT, 64 * NWV>;
+  using Ring = KeyRing<T, D, KT, NWV, NBUF>;
   constexpr int NC = D / MM::KSTEP;
   constexpr int NKB = KT / 16;
-  __shared__ __attribute__((aligned(16))) char lds[2 * KTile::BYTES];
-  __shared__ float red[2][NWV][KT];
+  // one LDS object: the ring, then the column partials red[NBUF][NWV][KT]
+  // (with a second object the compiler adds a full vmcnt wait before every
+  // read of the ring)
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * Ring::BYTES + NBUF * NWV * KT * 4];
+  float(*red)[NWV][KT] = reinterpret_cast<float(*)[NWV][KT]>(lds + NBUF * Ring::BYTES);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, qg = lane >> 4;
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const int nrb = cdiv(a.G * a.W, 16);
@@ -253,15 +354,16 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
 
   typename MM::frag qf[NC];
   load_q<T, D>(qf, a, bi, h, 16 * wave + col, qg);
-  float M[4], w[4];
-  bool ok[4];
+  int lt[Ring::KBP][Ring::NCL];
+  Ring::lane_terms(lt, col, qg);
+  float nM[4], w[4];  // -M and the weight 1/sum of each row (0, 0 past G*W)
   const size_t gidx = static_cast<size_t>(bi) * a.Hkv + h;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 16 * wave + 4 * qg + r;
-    ok[r] = row < a.G * a.W;
-    M[r] = ok[r] ? a.rowstat[2 * (gidx * a.Rg + row)] : 0.f;
-    w[r] = ok[r] ? a.rowstat[2 * (gidx * a.Rg + row) + 1] : 0.f;
+    const bool ok = row < a.G * a.W;
+    nM[r] = ok ? -a.rowstat[2 * (gidx * a.Rg + row)] : 0.f;
+    w[r] = ok ? a.rowstat[2 * (gidx * a.Rg + row) + 1] : 0.f;
   }
   const Prompt pr = prompt_of(a, bi, h);
   const int mend = pr.L - a.R;
@@ -269,39 +371,50 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
   if (pr.L <= a.C || k0 >= k1) return;  // stored as is / past the middle region
   const T* kbase = static_cast<const T*>(a.k) + pr.row0 * D;
   float* raw = a.raw + gidx * a.m - a.S;  // indexed by absolute key
+  const float sc = a.scale_log2;
+  // column sums of the tile at tb from partial buffer b: the NWV waves in order
+  auto columns_out = [&](int tb, int b) {
+    if (tid < KT && tb + tid < k1) {
+      float v = 0.f;
+      for (int wv = 0; wv < nrb; ++wv) v += red[b][wv][tid];
+      raw[tb + tid] = v;
+    }
+  };
 
-  u32x4_t ld[KTile::NLD];
-  KTile::load(ld, kbase, k0, k1, tid);
-  KTile::store(lds, ld, tid);
-  __syncthreads();
-  int t = 0;
-  for (int t0 = k0; t0 < k1; t0 += KT, ++t) {
-    const char* cur = lds + (t & 1) * KTile::BYTES;
-    const bool more = t0 + KT < k1;
-    if (more) KTile::load(ld, kbase, t0 + KT, k1, tid);
-    if (active) {
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    Ring::issue(lds + i * Ring::BYTES, kbase, k0 + i * KT, k1, wave, lane);
+  Ring::wait_all();
+  for (int base = k0; base < k1; base += NBUF * KT) {
+#pragma unroll
+    for (int sl = 0; sl < NBUF; ++sl) {  // tile at t0: ring slot and partial buffer sl
+      const int t0 = base + sl * KT;
+      if (t0 >= k1) break;
+      Ring::wait_barrier(wave);  // tile t0 in LDS; the previous tile's partials in red
+      Ring::issue(lds + ((sl + NBUF - 1) % NBUF) * Ring::BYTES, kbase, t0 + (NBUF - 1) * KT, k1,
+                  wave, lane);
+      if (t0 > k0) columns_out(t0 - KT, (sl + NBUF - 1) % NBUF);
+      if (!active) continue;
+      const char* cur = lds + sl * Ring::BYTES;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc = MM::mma(qf[c], KTile::bfrag(cur, kb, c, col, qg), acc);
+        for (int c = 0; c < NC; ++c) acc = MM::mma(qf[c], Ring::bfrag(cur, lt, kb, c), acc);
         float cs = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          cs += ok[r] ? fast_exp2(__builtin_fmaf(acc[r], a.scale_log2, -M[r])) * w[r] : 0.f;
-        cs = xor_sum(cs, 16);
-        cs = xor_sum(cs, 32);
-        if (qg == 0) red[t & 1][wave][16 * kb + col] = cs;
+          cs = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[r], sc, nM[r])), w[r], cs);
+        cs = sum_across_16(cs);
+        cs = sum_across_32(cs);
+        if (qg == 0) red[sl][wave][16 * kb + col] = cs;
       }
     }
-    if (more) KTile::store(lds + ((t + 1) & 1) * KTile::BYTES, ld, tid);
-    __syncthreads();
-    if (tid < KT && t0 + tid < k1) {
-      float v = 0.f;
-      for (int wv = 0; wv < nrb; ++wv) v += red[t & 1][wv][tid];
-      raw[t0 + tid] = v;
-    }
   }
+  Ring::drain();
+  __syncthreads();
+  const int last = (k1 - 1 - k0) / KT;  // the last tile, in partial buffer last % NBUF
+  columns_out(k0 + last * KT, last % NBUF);
 }
 
 // Build the cache rows of one request: slots [0, S) <- tokens 0..S-1, slots
@@ -369,18 +482,27 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
   }
 }
 
+// Ring depth: SS_SCORE_NBUF slots, fewer where they would not fit in LDS.
+template <typename T, int D, int KT, int NWV>
+constexpr int score_nbuf() {
+  constexpr int bytes = KeyRing<T, D, KT, NWV, 2>::BYTES;
+  constexpr int fit = (SCORE_LDS_BUDGET - 2 * NWV * KT * 4) / bytes;
+  return SCORE_NBUF < fit ? SCORE_NBUF : fit;
+}
+
 template <typename T, int D, int KT, int NWV>
 hipError_t run_scores_w(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  constexpr int NB = score_nbuf<T, D, KT, NWV>();
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
   const size_t rows = static_cast<size_t>(a.b) * a.Hkv * a.Rg;
   const unsigned rgrid = static_cast<unsigned>(cdiv(static_cast<int>(rows), 256));
   if (a.lse != nullptr) {
     lse_rowstat_kernel<<<rgrid, 256, 0, st>>>(a);
   } else {
-    score_rowstat_kernel<T, D, KT, NWV><<<dim3(a.n_chunk1, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
+    score_rowstat_kernel<T, D, KT, NWV, NB><<<dim3(a.n_chunk1, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
     score_rowstat_combine_kernel<<<rgrid, 256, 0, st>>>(a);
   }
-  score_columns_kernel<T, D, KT, NWV><<<dim3(a.n_chunk2, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
+  score_columns_kernel<T, D, KT, NWV, NB><<<dim3(a.n_chunk2, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -400,6 +522,44 @@ hipError_t run_gather(bool compressed, const PrefillArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+namespace {
+
+template <typename T, int D, int KT, int NWV>
+hipError_t score_slots_w(int* slots1, int* slots2) {
+  constexpr int NB = score_nbuf<T, D, KT, NWV>();
+  int dev = 0, cus = 0, b1 = 0, b2 = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &b1, reinterpret_cast<const void*>(score_rowstat_kernel<T, D, KT, NWV, NB>), 64 * NWV, 0);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &b2, reinterpret_cast<const void*>(score_columns_kernel<T, D, KT, NWV, NB>), 64 * NWV, 0);
+  if (e != hipSuccess) return e;
+  *slots1 = cus * b1;
+  *slots2 = cus * b2;
+  return (*slots1 > 0 && *slots2 > 0) ? hipSuccess : hipErrorInvalidValue;
+}
+
+template <typename T, int D, int KT>
+hipError_t score_slots(int Rg, int* slots1, int* slots2) {
+  if (Rg <= 128) return score_slots_w<T, D, KT, 8>(slots1, slots2);
+  if (Rg <= 256) return score_slots_w<T, D, KT, 16>(slots1, slots2);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t prefill_score_slots(int dtype, int D, int Rg, int* slots1, int* slots2) {
+  if (dtype == 0 && D == 64) return score_slots<float, 64, 64>(Rg, slots1, slots2);
+  if (dtype == 0 && D == 128) return score_slots<float, 128, 64>(Rg, slots1, slots2);
+  if (dtype == 1 && D == 64) return score_slots<bf16_t, 64, 64>(Rg, slots1, slots2);
+  if (dtype == 1 && D == 128) return score_slots<bf16_t, 128, 64>(Rg, slots1, slots2);
+  if (dtype == 1 && D == 576) return score_slots_w<bf16_t, 576, 32, 16>(slots1, slots2);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStream_t st,
                                  hipEvent_t ev0, hipEvent_t ev1) {

@@ -24,8 +24,8 @@ def _mla(**kw):
 
 
 def test_mla_prefill_small_ragged():
-    # L = 4999: 3 row-stat chunks (2048) with a ragged tail; m = 4999 - 16 - 512
-    # = 4471 middle keys (column chunks of 1024, last tile of 55 keys)
+    # L = 4999 keys (several chunks, ragged tail); m = 4999 - 16 - 512 = 4471
+    # middle keys (32-key tiles: last tile of 23 keys)
     prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512), 21, L=4999)
 
 

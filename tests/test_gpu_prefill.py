@@ -25,8 +25,9 @@ def test_prefill_uncompressed_is_identity(L):
 
 @pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "bf16"), (128, "f32")])
 def test_prefill_small_ragged(d, dtype):
-    # several key tiles and chunks with ragged tails: L = 4999 (chunk1 2048),
-    # m = 4999 - 16 - 512 = 4471 (chunk2 1024, tile 64 -> tail 55)
+    # several key tiles and chunks with ragged tails: L = 4999 keys in pass 1,
+    # m = 4999 - 16 - 512 = 4471 middle keys in pass 2 (64-key tiles: tails of
+    # 7 and 55 keys; the chunk lengths follow the device's workgroup slots)
     w = synth.workload("llama8b_c4k", B=2, d_qk=d, d_v=d, rope_end=d, dtype=dtype, L_sink=16,
                        K=200, L_recent=512)
     prefill_case(w, 4, L=4999)
