@@ -8,12 +8,15 @@
 // ascending), written in ascending index order.
 //
 // One 1024-thread workgroup per group.  Scores are non-negative floats, so
-// their bit patterns order like the values.  A 3-pass radix select
-// (11 + 11 + 10 bits, LDS histograms) finds the K-th largest value T and how
-// many of the keys equal to T are kept (the lowest-indexed ones); an ordered
-// compaction (ballot + popcount per wave, wave order across the group) then
-// writes the kept indices ascending.  Integer work only after the pooling
-// max, so the result is exact for the given scores.
+// their bit patterns order like the values (bit 31 is 0).  The raw scores are
+// staged through LDS in chunks for the pooling; the pooled scores stay in LDS
+// when the group has at most KEEP of them (else they are re-read from the
+// pooled output).  A 3-pass radix select (bits 30..20, 19..9, 8..0, LDS
+// histograms) finds the K-th largest value T and how many of the keys equal
+// to T are kept (the lowest-indexed ones); an ordered compaction (ballot +
+// popcount per wave, wave order across the group) then writes the kept
+// indices ascending.  Integer work only after the pooling max, so the result
+// is exact for the given scores.
 #include "common.h"
 #include "launch.h"
 
@@ -23,6 +26,10 @@ namespace {
 
 constexpr int NT = 1024;
 constexpr int NW = NT / 64;
+constexpr int KEEP = 16384;  // pooled scores held in LDS
+constexpr int CH = 16384;    // raw scores pooled per LDS chunk
+constexpr int PMAX = 256;    // largest pooling half-width staged in LDS
+constexpr int UNR = 16;      // loads in flight per thread in the global passes
 
 // Inclusive prefix sum over the 1024 threads of the workgroup.
 __device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* wsum) {
@@ -69,7 +76,31 @@ __device__ __forceinline__ void pick_bin(const uint32_t* hist, int nb, uint32_t*
   __syncthreads();
 }
 
+// f(v) for every pooled score v of the group: from LDS (kept) or from the
+// pooled output, UNR loads in flight per thread.
+template <typename F>
+__device__ __forceinline__ void for_pooled(bool kept, const uint32_t* keep, const uint32_t* pbits,
+                                           int m, F&& f) {
+  if (kept) {
+    for (int i = threadIdx.x; i < m; i += NT) f(keep[i]);
+    return;
+  }
+  for (int i0 = threadIdx.x; i0 < m; i0 += UNR * NT) {
+    uint32_t v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = i0 + u * NT;
+      v[u] = i < m ? pbits[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (i0 + u * NT < m) f(v[u]);
+  }
+}
+
 __global__ __launch_bounds__(NT) void pool_select_kernel(PrefillArgs a) {
+  __shared__ uint32_t keep[KEEP];
+  __shared__ float stage[CH + 2 * PMAX];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t wsum[NW];
   __shared__ uint32_t sh_digit, sh_krem;
@@ -85,56 +116,96 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(PrefillArgs a) {
   const float* raw = a.raw + g * a.m;
   float* pooled = a.pooled + g * a.m;
   const uint32_t* pbits = reinterpret_cast<const uint32_t*>(pooled);
+  const bool kept = m <= KEEP;
 
   for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
-  __syncthreads();
-  // pooling + histogram of bits [31:21]
-  for (int i = tid; i < m; i += NT) {
-    const int lo = max(0, i - p), hi = min(m - 1, i + p);
-    float v = raw[lo];
-    for (int u = lo + 1; u <= hi; ++u) v = fmaxf(v, raw[u]);
+  // pooling + histogram of bits [30:20]
+  auto pool_out = [&](int i, float v) {
     pooled[i] = v;
-    atomicAdd(&hist[__float_as_uint(v) >> 21], 1u);
+    const uint32_t b = __float_as_uint(v);
+    if (kept) keep[i] = b;
+    atomicAdd(&hist[b >> 20], 1u);
+  };
+  if (p <= PMAX) {
+    for (int c0 = 0; c0 < m; c0 += CH) {
+      const int s0 = max(0, c0 - p), s1 = min(m, c0 + CH + p);  // staged raw[s0, s1)
+      __syncthreads();  // the previous chunk's reads of stage are done (and hist is clear)
+      for (int i0 = s0 + tid; i0 < s1; i0 += UNR * NT) {  // UNR loads in flight
+        float v[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) v[u] = i0 + u * NT < s1 ? raw[i0 + u * NT] : 0.f;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+          if (i0 + u * NT < s1) stage[i0 + u * NT - s0] = v[u];
+      }
+      __syncthreads();
+      for (int i = c0 + tid; i < min(m, c0 + CH); i += NT) {
+        const int lo = max(0, i - p), hi = min(m - 1, i + p);
+        float v = stage[lo - s0];
+        for (int u = lo + 1; u <= hi; ++u) v = fmaxf(v, stage[u - s0]);
+        pool_out(i, v);
+      }
+    }
+  } else {
+    __syncthreads();
+    for (int i = tid; i < m; i += NT) {
+      const int lo = max(0, i - p), hi = min(m - 1, i + p);
+      float v = raw[lo];
+      for (int u = lo + 1; u <= hi; ++u) v = fmaxf(v, raw[u]);
+      pool_out(i, v);
+    }
   }
   __syncthreads();
   if (K == 0) return;
   pick_bin(hist, 2048, wsum, &sh_digit, &sh_krem, static_cast<uint32_t>(K));
-  uint32_t prefix = sh_digit << 21;
+  uint32_t prefix = sh_digit << 20;
   uint32_t krem = sh_krem;
 
-  // bits [20:10] among keys whose bits [31:21] match
+  // bits [19:9] among keys whose bits [30:20] match (a kept pooled score is
+  // visible to every thread after the barriers in pick_bin; one re-read from
+  // the pooled output needs this workgroup's own stores, which it sees)
   for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < m; i += NT) {
-    const uint32_t v = pbits[i];
-    if ((v >> 21) == (prefix >> 21)) atomicAdd(&hist[(v >> 10) & 0x7ffu], 1u);
-  }
+  for_pooled(kept, keep, pbits, m, [&](uint32_t v) {
+    if ((v >> 20) == (prefix >> 20)) atomicAdd(&hist[(v >> 9) & 0x7ffu], 1u);
+  });
   __syncthreads();
   pick_bin(hist, 2048, wsum, &sh_digit, &sh_krem, krem);
-  prefix |= sh_digit << 10;
+  prefix |= sh_digit << 9;
   krem = sh_krem;
 
-  // bits [9:0] among keys whose bits [31:10] match
-  for (int i = tid; i < 1024; i += NT) hist[i] = 0u;
+  // bits [8:0] among keys whose bits [30:9] match
+  for (int i = tid; i < 512; i += NT) hist[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < m; i += NT) {
-    const uint32_t v = pbits[i];
-    if ((v >> 10) == (prefix >> 10)) atomicAdd(&hist[v & 0x3ffu], 1u);
-  }
+  for_pooled(kept, keep, pbits, m, [&](uint32_t v) {
+    if ((v >> 9) == (prefix >> 9)) atomicAdd(&hist[v & 0x1ffu], 1u);
+  });
   __syncthreads();
-  pick_bin(hist, 1024, wsum, &sh_digit, &sh_krem, krem);
+  pick_bin(hist, 512, wsum, &sh_digit, &sh_krem, krem);
   const uint32_t T = prefix | sh_digit;
   const uint32_t need_eq = sh_krem;  // keys equal to T that are kept (lowest indices)
 
-  // ordered compaction: wave w scans [w*seg, (w+1)*seg)
+  // ordered compaction: wave w scans [w*seg, (w+1)*seg), UNR rows of 64
+  // scores per batch of loads
   const int seg = cdiv(cdiv(m, NW), 64) * 64;
   const int beg = wave * seg, end = min(beg + seg, m);
+  auto load_rows = [&](int base, uint32_t (&v)[UNR]) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + 64 * u + lane;
+      v[u] = i < end ? (kept ? keep[i] : pbits[i]) : 0u;
+    }
+  };
   uint32_t ngt = 0, neq = 0;
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    const uint32_t v = i < end ? pbits[i] : 0u;
-    ngt += __popcll(__ballot(i < end && v > T));
-    neq += __popcll(__ballot(i < end && v == T));
+  for (int base = beg; base < end; base += 64 * UNR) {
+    uint32_t v[UNR];
+    load_rows(base, v);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const bool in = base + 64 * u + lane < end;
+      ngt += __popcll(__ballot(in && v[u] > T));
+      neq += __popcll(__ballot(in && v[u] == T));
+    }
   }
   if (lane == 0) {
     cnt_gt[wave] = ngt;
@@ -155,18 +226,22 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(PrefillArgs a) {
   uint32_t eq_run = eq_before[wave], out_run = out_before[wave];
   const unsigned long long below = (1ull << lane) - 1ull;
   int32_t* sel = a.sel + g * K;
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    const uint32_t v = i < end ? pbits[i] : 0u;
-    const bool gt = i < end && v > T;
-    const bool eq = i < end && v == T;
-    const unsigned long long eqm = __ballot(eq);
-    const bool take = gt || (eq && eq_run + __popcll(eqm & below) < need_eq);
-    const unsigned long long tm = __ballot(take);
-    const uint32_t at = out_run + __popcll(tm & below);
-    if (take && at < static_cast<uint32_t>(K)) sel[at] = i;
-    eq_run += __popcll(eqm);
-    out_run += __popcll(tm);
+  for (int base = beg; base < end; base += 64 * UNR) {
+    uint32_t v[UNR];
+    load_rows(base, v);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + 64 * u + lane;
+      const bool gt = i < end && v[u] > T;
+      const bool eq = i < end && v[u] == T;
+      const unsigned long long eqm = __ballot(eq);
+      const bool take = gt || (eq && eq_run + __popcll(eqm & below) < need_eq);
+      const unsigned long long tm = __ballot(take);
+      const uint32_t at = out_run + __popcll(tm & below);
+      if (take && at < static_cast<uint32_t>(K)) sel[at] = i;
+      eq_run += __popcll(eqm);
+      out_run += __popcll(tm);
+    }
   }
 }
 
