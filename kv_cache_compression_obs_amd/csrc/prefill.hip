@@ -153,14 +153,16 @@ __device__ __forceinline__ void load_q(typename Mma<T>::frag (&qf)[D / Mma<T>::K
                : Mma<T>::zero();
 }
 
-// Pass 1.  Grid (n_chunk1, Hkv, b), NWV waves.  Wave w owns rows 16w .. 16w+15
-// of the group; accumulator lane (col, qg) register r holds row 16w + 4qg + r
-// and key 16kb + col of the tile.  Each lane keeps, per row, a reference
-// maximum m (log2 units) and the sum of 2^(x - m) over the keys it sees; the
-// 16 lanes of a row are merged at the end.  m is raised only when a tile's
-// maximum exceeds it by more than 2^LAZY, so the terms stay below 2^LAZY and
-// the rescale (one exp2 per row) is skipped by the whole wave on most tiles.
-template <typename T, int D, int KT, int NWV, int NBUF>
+// Pass 1.  Grid (n_chunk1, Hkv, b), NWV waves of RB row blocks.  Wave w owns
+// rows 16*RB*w .. 16*RB*(w+1)-1 of the group, as RB blocks of 16 that share
+// every key fragment read from LDS; in block rb the accumulator lane
+// (col, qg) register r holds row 16*(RB*w + rb) + 4qg + r and key 16kb + col
+// of the tile.  Each lane keeps, per row, a reference maximum m (log2 units)
+// and the sum of 2^(x - m) over the keys it sees; the 16 lanes of a row are
+// merged at the end.  m is raised only when a tile's maximum exceeds it by
+// more than 2^LAZY, so the terms stay below 2^LAZY and the rescale (one exp2
+// per row) is skipped by the whole wave on most tiles.
+template <typename T, int D, int KT, int NWV, int NBUF, int RB>
 __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) {
   using MM = Mma<T>;
   using Ring = KeyRing<T, D, KT, NWV, NBUF>;
@@ -174,12 +176,13 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, qg = lane >> 4;
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
-  const bool active = 16 * wave < a.G * a.W;  // wave-uniform
+  const bool active = 16 * RB * wave < a.G * a.W;  // wave-uniform
   const Prompt pr = prompt_of(a, bi, h);
   if (pr.L <= a.C || chunk * a.chunk1 >= pr.L) return;  // stored as is / past the prompt
 
-  typename MM::frag qf[NC];
-  load_q<T, D>(qf, a, bi, h, 16 * wave + col, qg);
+  typename MM::frag qf[RB][NC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) load_q<T, D>(qf[rb], a, bi, h, 16 * (RB * wave + rb) + col, qg);
   int lt[Ring::KBP][Ring::NCL];
   Ring::lane_terms(lt, col, qg);
   const int k0 = chunk * a.chunk1, k1 = min(k0 + a.chunk1, pr.L);
@@ -187,13 +190,15 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
 
   const float sc = a.scale_log2;
   const float lazy_raw = LAZY / sc;  // LAZY in raw dot-product units
-  float m[4], s[4], thr[4];
+  float m[RB][4], s[RB][4], thr[RB][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = EMPTY;
-    s[r] = 0.f;
-    thr[r] = -INFINITY;  // the first visible key raises m
-  }
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m[rb][r] = EMPTY;
+      s[rb][r] = 0.f;
+      thr[rb][r] = -INFINITY;  // the first visible key raises m
+    }
   // keys of a tile wholly below this bound are visible to every row and real
   const int open_end = min(k1, pr.L - a.W + 1);
   // the first NBUF - 1 tiles in flight; each step then refills the slot its
@@ -212,76 +217,92 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
                   wave, lane);
       if (!active) continue;
       const char* cur = lds + sl * Ring::BYTES;
-      f32x4_t acc[NKB];
+      f32x4_t acc[RB][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        acc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          acc[kb] = MM::mma(qf[c], Ring::bfrag(cur, lt, kb, c), acc[kb]);
+        for (int rb = 0; rb < RB; ++rb) acc[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const typename MM::frag kf = Ring::bfrag(cur, lt, kb, c);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[rb][kb] = MM::mma(qf[rb][c], kf, acc[rb][kb]);
+        }
       }
       if (t0 + KT > open_end) {  // (uniform) the ragged end or the causal window
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * wave + 4 * qg + r;
-          const int lim = row < a.G * a.W ? pr.L - a.W + row % a.W : -1;  // last visible key
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const int key = t0 + 16 * kb + col;
-            if (!(key < k1 && key <= lim)) acc[kb][r] = -INFINITY;
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * (RB * wave + rb) + 4 * qg + r;
+            const int lim = row < a.G * a.W ? pr.L - a.W + row % a.W : -1;  // last visible key
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+              const int key = t0 + 16 * kb + col;
+              if (!(key < k1 && key <= lim)) acc[rb][kb][r] = -INFINITY;
+            }
           }
-        }
       }
       // raise m when the tile's largest raw dot product passes thr, the
       // raw-units image of m + LAZY
-      auto tile_max = [&](int r) {
-        float tm = acc[0][r];
+      auto tile_max = [&](int rb, int r) {
+        float tm = acc[rb][0][r];
 #pragma unroll
-        for (int kb = 1; kb < NKB; ++kb) tm = fmaxf(tm, acc[kb][r]);
+        for (int kb = 1; kb < NKB; ++kb) tm = fmaxf(tm, acc[rb][kb][r]);
         return tm;
       };
       bool raise = false;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) raise |= tile_max(r) > thr[r];
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) raise |= tile_max(rb, r) > thr[rb][r];
       if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform; rare once m settles
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float tm = tile_max(r);
-          if (tm > thr[r]) {
-            const float mn = tm * sc;
-            s[r] *= fast_exp2(m[r] - mn);
-            m[r] = mn;
-            thr[r] = tm + lazy_raw;
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float tm = tile_max(rb, r);
+            if (tm > thr[rb][r]) {
+              const float mn = tm * sc;
+              s[rb][r] *= fast_exp2(m[rb][r] - mn);
+              m[rb][r] = mn;
+              thr[rb][r] = tm + lazy_raw;
+            }
           }
-        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[r] += fast_exp2(__builtin_fmaf(acc[kb][r], sc, -m[r]));
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            s[rb][r] += fast_exp2(__builtin_fmaf(acc[rb][kb][r], sc, -m[rb][r]));
     }
   }
   Ring::drain();
   if (!active) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float M = m[r];
-    M = xor_max(M, 1);
-    M = xor_max(M, 2);
-    M = xor_max(M, 4);
-    M = xor_max(M, 8);
-    float sv = s[r] * fast_exp2(m[r] - M);
-    sv = xor_sum(sv, 1);
-    sv = xor_sum(sv, 2);
-    sv = xor_sum(sv, 4);
-    sv = xor_sum(sv, 8);
-    const int row = 16 * wave + 4 * qg + r;
-    if (col == 0 && row < a.Rg) {
-      const size_t idx = ((static_cast<size_t>(bi) * a.Hkv + h) * a.Rg + row) * a.n_chunk1 + chunk;
-      a.part1[2 * idx] = M == EMPTY ? -INFINITY : M;
-      a.part1[2 * idx + 1] = sv;
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float M = m[rb][r];
+      M = xor_max(M, 1);
+      M = xor_max(M, 2);
+      M = xor_max(M, 4);
+      M = xor_max(M, 8);
+      float sv = s[rb][r] * fast_exp2(m[rb][r] - M);
+      sv = xor_sum(sv, 1);
+      sv = xor_sum(sv, 2);
+      sv = xor_sum(sv, 4);
+      sv = xor_sum(sv, 8);
+      const int row = 16 * (RB * wave + rb) + 4 * qg + r;
+      if (col == 0 && row < a.Rg) {
+        const size_t idx =
+            ((static_cast<size_t>(bi) * a.Hkv + h) * a.Rg + row) * a.n_chunk1 + chunk;
+        a.part1[2 * idx] = M == EMPTY ? -INFINITY : M;
+        a.part1[2 * idx + 1] = sv;
+      }
     }
-  }
 }
 
 // Merge the per-chunk (max, sum) of every query row in fp64.
@@ -329,11 +350,12 @@ __global__ __launch_bounds__(256) void lse_rowstat_kernel(PrefillArgs a) {
 
 // Pass 2.  Grid (n_chunk2, Hkv, b) over the middle keys [S, L-R).  Every
 // middle key is visible to every observation row (the window lies inside the
-// recent region), so no causal mask.  Column sums: 4 rows in registers, then
-// the 4 lane groups (lane swaps across 16 and 32), then the NWV waves through
-// LDS in wave order.  Rows past G*W have zero queries and weight 0, so they
-// add exact zeros.
-template <typename T, int D, int KT, int NWV, int NBUF>
+// recent region), so no causal mask.  Rows as in pass 1 (RB blocks of 16 per
+// wave).  Column sums: the RB*4 rows of a lane in registers, then the 4 lane
+// groups (lane swaps across 16 and 32), then the NWV waves through LDS in
+// wave order.  Rows past G*W have zero queries and weight 0, so they add
+// exact zeros.
+template <typename T, int D, int KT, int NWV, int NBUF, int RB>
 __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) {
   using MM = Mma<T>;
   using Ring = KeyRing<T, D, KT, NWV, NBUF>;
@@ -349,22 +371,25 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, qg = lane >> 4;
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
-  const int nrb = cdiv(a.G * a.W, 16);
-  const bool active = wave < nrb;
+  const int nwa = cdiv(a.G * a.W, 16 * RB);  // waves holding real rows
+  const bool active = wave < nwa;
 
-  typename MM::frag qf[NC];
-  load_q<T, D>(qf, a, bi, h, 16 * wave + col, qg);
+  typename MM::frag qf[RB][NC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) load_q<T, D>(qf[rb], a, bi, h, 16 * (RB * wave + rb) + col, qg);
   int lt[Ring::KBP][Ring::NCL];
   Ring::lane_terms(lt, col, qg);
-  float nM[4], w[4];  // -M and the weight 1/sum of each row (0, 0 past G*W)
+  float nM[RB][4], w[RB][4];  // -M and the weight 1/sum of each row (0, 0 past G*W)
   const size_t gidx = static_cast<size_t>(bi) * a.Hkv + h;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 16 * wave + 4 * qg + r;
-    const bool ok = row < a.G * a.W;
-    nM[r] = ok ? -a.rowstat[2 * (gidx * a.Rg + row)] : 0.f;
-    w[r] = ok ? a.rowstat[2 * (gidx * a.Rg + row) + 1] : 0.f;
-  }
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * (RB * wave + rb) + 4 * qg + r;
+      const bool ok = row < a.G * a.W;
+      nM[rb][r] = ok ? -a.rowstat[2 * (gidx * a.Rg + row)] : 0.f;
+      w[rb][r] = ok ? a.rowstat[2 * (gidx * a.Rg + row) + 1] : 0.f;
+    }
   const Prompt pr = prompt_of(a, bi, h);
   const int mend = pr.L - a.R;
   const int k0 = a.S + chunk * a.chunk2, k1 = min(k0 + a.chunk2, mend);
@@ -372,11 +397,11 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
   const T* kbase = static_cast<const T*>(a.k) + pr.row0 * D;
   float* raw = a.raw + gidx * a.m - a.S;  // indexed by absolute key
   const float sc = a.scale_log2;
-  // column sums of the tile at tb from partial buffer b: the NWV waves in order
+  // column sums of the tile at tb from partial buffer b: the waves in order
   auto columns_out = [&](int tb, int b) {
     if (tid < KT && tb + tid < k1) {
       float v = 0.f;
-      for (int wv = 0; wv < nrb; ++wv) v += red[b][wv][tid];
+      for (int wv = 0; wv < nwa; ++wv) v += red[b][wv][tid];
       raw[tb + tid] = v;
     }
   };
@@ -398,13 +423,22 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
       const char* cur = lds + sl * Ring::BYTES;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc[RB];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc = MM::mma(qf[c], Ring::bfrag(cur, lt, kb, c), acc);
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const typename MM::frag kf = Ring::bfrag(cur, lt, kb, c);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[rb] = MM::mma(qf[rb][c], kf, acc[rb]);
+        }
         float cs = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          cs = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[r], sc, nM[r])), w[r], cs);
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            cs = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[rb][r], sc, nM[rb][r])), w[rb][r],
+                                cs);
         cs = sum_across_16(cs);
         cs = sum_across_32(cs);
         if (qg == 0) red[sl][wave][16 * kb + col] = cs;
@@ -486,11 +520,11 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
 template <typename T, int D, int KT, int NWV>
 constexpr int score_nbuf() {
   constexpr int bytes = KeyRing<T, D, KT, NWV, 2>::BYTES;
-  constexpr int fit = (SCORE_LDS_BUDGET - 2 * NWV * KT * 4) / bytes;
+  constexpr int fit = SCORE_LDS_BUDGET / (bytes + NWV * KT * 4);  // a ring slot + its partials
   return SCORE_NBUF < fit ? SCORE_NBUF : fit;
 }
 
-template <typename T, int D, int KT, int NWV>
+template <typename T, int D, int KT, int NWV, int RB>
 hipError_t run_scores_w(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int NB = score_nbuf<T, D, KT, NWV>();
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
@@ -499,19 +533,23 @@ hipError_t run_scores_w(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hi
   if (a.lse != nullptr) {
     lse_rowstat_kernel<<<rgrid, 256, 0, st>>>(a);
   } else {
-    score_rowstat_kernel<T, D, KT, NWV, NB><<<dim3(a.n_chunk1, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
+    score_rowstat_kernel<T, D, KT, NWV, NB, RB>
+        <<<dim3(a.n_chunk1, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
     score_rowstat_combine_kernel<<<rgrid, 256, 0, st>>>(a);
   }
-  score_columns_kernel<T, D, KT, NWV, NB><<<dim3(a.n_chunk2, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
+  score_columns_kernel<T, D, KT, NWV, NB, RB>
+      <<<dim3(a.n_chunk2, a.Hkv, a.b), 64 * NWV, 0, st>>>(a);
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 // One 16-row block per wave: 8 waves cover G*W <= 128 rows, 16 waves <= 256.
+// (The latent shape uses 8 waves of two blocks each: every key fragment read
+// from LDS then feeds two MFMAs, halving the LDS reads that bound it.)
 template <typename T, int D, int KT>
 hipError_t run_scores(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  if (a.Rg <= 128) return run_scores_w<T, D, KT, 8>(a, st, ev0, ev1);
-  if (a.Rg <= 256) return run_scores_w<T, D, KT, 16>(a, st, ev0, ev1);
+  if (a.Rg <= 128) return run_scores_w<T, D, KT, 8, 1>(a, st, ev0, ev1);
+  if (a.Rg <= 256) return run_scores_w<T, D, KT, 16, 1>(a, st, ev0, ev1);
   return hipErrorInvalidValue;
 }
 
@@ -525,7 +563,7 @@ hipError_t run_gather(bool compressed, const PrefillArgs& a, hipStream_t st) {
 
 namespace {
 
-template <typename T, int D, int KT, int NWV>
+template <typename T, int D, int KT, int NWV, int RB>
 hipError_t score_slots_w(int* slots1, int* slots2) {
   constexpr int NB = score_nbuf<T, D, KT, NWV>();
   int dev = 0, cus = 0, b1 = 0, b2 = 0;
@@ -533,10 +571,12 @@ hipError_t score_slots_w(int* slots1, int* slots2) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &b1, reinterpret_cast<const void*>(score_rowstat_kernel<T, D, KT, NWV, NB>), 64 * NWV, 0);
+        &b1, reinterpret_cast<const void*>(score_rowstat_kernel<T, D, KT, NWV, NB, RB>), 64 * NWV,
+        0);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &b2, reinterpret_cast<const void*>(score_columns_kernel<T, D, KT, NWV, NB>), 64 * NWV, 0);
+        &b2, reinterpret_cast<const void*>(score_columns_kernel<T, D, KT, NWV, NB, RB>), 64 * NWV,
+        0);
   if (e != hipSuccess) return e;
   *slots1 = cus * b1;
   *slots2 = cus * b2;
@@ -545,8 +585,8 @@ hipError_t score_slots_w(int* slots1, int* slots2) {
 
 template <typename T, int D, int KT>
 hipError_t score_slots(int Rg, int* slots1, int* slots2) {
-  if (Rg <= 128) return score_slots_w<T, D, KT, 8>(slots1, slots2);
-  if (Rg <= 256) return score_slots_w<T, D, KT, 16>(slots1, slots2);
+  if (Rg <= 128) return score_slots_w<T, D, KT, 8, 1>(slots1, slots2);
+  if (Rg <= 256) return score_slots_w<T, D, KT, 16, 1>(slots1, slots2);
   return hipErrorInvalidValue;
 }
 
@@ -557,7 +597,7 @@ hipError_t prefill_score_slots(int dtype, int D, int Rg, int* slots1, int* slots
   if (dtype == 0 && D == 128) return score_slots<float, 128, 64>(Rg, slots1, slots2);
   if (dtype == 1 && D == 64) return score_slots<bf16_t, 64, 64>(Rg, slots1, slots2);
   if (dtype == 1 && D == 128) return score_slots<bf16_t, 128, 64>(Rg, slots1, slots2);
-  if (dtype == 1 && D == 576) return score_slots_w<bf16_t, 576, 32, 16>(slots1, slots2);
+  if (dtype == 1 && D == 576) return score_slots_w<bf16_t, 576, 32, 8, 2>(slots1, slots2);
   return hipErrorInvalidValue;
 }
 
@@ -567,7 +607,7 @@ hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStre
   if (dtype == 0 && D == 128) return run_scores<float, 128, 64>(a, st, ev0, ev1);
   if (dtype == 1 && D == 64) return run_scores<bf16_t, 64, 64>(a, st, ev0, ev1);
   if (dtype == 1 && D == 128) return run_scores<bf16_t, 128, 64>(a, st, ev0, ev1);
-  if (dtype == 1 && D == 576) return run_scores_w<bf16_t, 576, 32, 16>(a, st, ev0, ev1);
+  if (dtype == 1 && D == 576) return run_scores_w<bf16_t, 576, 32, 8, 2>(a, st, ev0, ev1);
   return hipErrorInvalidValue;
 }
 
