@@ -1,9 +1,10 @@
 """GPU parity on the degenerate and boundary configurations of the method:
 no middle budget (K = 0), no sinks (L_sink = 0), no pooling (pool = 1), a
 one-query observation window (W = 1), plain multi-head attention (G = 1), the
-largest group the score kernels take (G = 16, G*W = 256 rows), and rotary
+largest group the score kernels take (G = 16, G*W = 256 rows), rotary
 embedding over part of the head (decode rotates dims 32..95 of 128) or over
-every dim of an fp32 head.  Each configuration runs the prefill comparison
+every dim of an fp32 head, and pooling windows at and past the select
+kernel's LDS staging limit or wider than the whole middle region.  Each configuration runs the prefill comparison
 (scores, selection, slot map, gathered rows) and a decode run across the ring
 wrap (outputs, written rows, n_tokens) against the oracle."""
 import pytest
@@ -27,6 +28,12 @@ CASES = {
                                       L_recent=512), 3000),
     "partial_rope": (SMALL, dict(B=2, rope_begin=32, rope_end=96, L_sink=16, K=200,
                                  L_recent=512), 3000),
+    # pooling half-width at the LDS-staged limit (256) and past it (the select
+    # kernel then pools straight from the raw scores); a window wider than the
+    # middle region makes every pooled score the maximum (all ties)
+    "pool_513_staged_limit": (SMALL, dict(B=2, pool=513, L_sink=16, K=200, L_recent=512), 3000),
+    "pool_515_unstaged": (SMALL, dict(B=2, pool=515, L_sink=16, K=200, L_recent=512), 3000),
+    "pool_wider_than_middle": (TINY, dict(pool=801), 512),
 }
 
 
