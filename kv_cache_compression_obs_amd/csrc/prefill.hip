@@ -9,15 +9,16 @@
 // Score of middle key i = sum over the G q-heads of the kv-head and the W
 // observation queries of that query's causal softmax probability of key i.
 // Two passes over the keys, both a dense Q_obs . K^T contraction on MFMA:
-//   pass 1 (score_rowstat): per query row, running max and sum of 2^x over
-//            key chunks, x = scale*log2(e) * q.k; combined in fp64 across
-//            chunks (score_rowstat_combine) into (max M, weight w = 1/sum);
+//   pass 1 (score_rowstat): per query row and chunk of keys, a reference
+//            maximum m and the sum of 2^(x - m), x = scale*log2(e) * q.k;
+//            combined in fp64 across chunks (score_rowstat_combine) into
+//            (M, weight w = 1/sum of 2^(x - M));
 //   pass 2 (score_columns): over the middle keys only, recompute x and sum
 //            2^(x - M) * w over the rows of the group, per key.
-// Both passes form x - M with the same fma (x = scale*log2(e) * q.k), so pass 2
-// sees the logits pass 1 normalised.  Exponentials use the hardware exp2
-// (fast_exp2): results below 2^-126 of a row's maximum flush to zero, a
-// negligible share of a sum whose largest term is 1.
+// Both passes form the exponent with one fma of the raw dot product
+// (fma(q.k, scale*log2(e), -m)).  Exponentials use the hardware exp2
+// (fast_exp2): results below 2^-126 flush to zero, a negligible share of a
+// sum whose largest term is at least 1.
 #include "common.h"
 #include "launch.h"
 
