@@ -231,6 +231,57 @@ def varlen_admission(ss, torch, synth, w, cfg, reps=5):
     return out
 
 
+def continuous_batching_decode(ss, torch, synth, steps=64, reps=2):
+    """Decode over the continuous-batching shape (64 rows of 32q/8kv, d 128,
+    bf16, C = 32768) holding requests of log-uniform lengths in [1k, 128k]
+    (seeded): rows below capacity attend over fewer slots, so the workgroups
+    of one launch carry very different amounts of work.  The cache contents
+    are random (timing only); n_tokens holds each request's length.  Two
+    cache copies alternate, so no launch reads what the previous one left in
+    the caches."""
+    w = synth.workload("llama8b_cb64")
+    cfg = ss.make_config(**w)
+    B, C, Hkv, d = w["B"], w["C"], w["n_kv_heads"], w["d_qk"]
+    lens = synth.request_lengths(w, 5, B)
+    caches = [ss.Cache(cfg, B) for _ in range(2)]
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for c in caches:
+        c.k.normal_(generator=g)
+        c.v.normal_(generator=g)
+    dec = synth.decode_inputs(w, 5, 8, device="cuda")
+    out = torch.empty(B, w["n_q_heads"], d, dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = ss.decode_workspace(cfg, B)
+    pos0 = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    posbuf = [pos0 + t for t in range(steps)]
+    us = []
+    for _ in range(reps):
+        for c in caches:
+            c.n_tokens.copy_(pos0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for t in range(steps):
+            ss.ss_decode_step(cfg, dec["q"][t % 8], dec["k_new"][t % 8], dec["v_new"][t % 8],
+                              posbuf[t // 2], caches[t % 2], out, err, ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us.append(ev[0].elapsed_time(ev[1]) * 1e3 / steps)
+    if int(err.item()) != 0:
+        raise RuntimeError("continuous-batching decode: pos != n_tokens")
+    step_us = min(us)
+    # slots attended per launch, averaged over the run (pos advances every
+    # second launch)
+    valid = sum(min(n + t // 2 + 1, C) for t in range(steps) for n in lens) / steps
+    bytes_step = valid * Hkv * 2 * d * 2
+    return {"rows": B, "cache_slots": C, "length_range": [min(lens), max(lens)],
+            "rows_at_capacity": sum(n >= C for n in lens),
+            "valid_slot_fraction": round(valid / (B * C), 4),
+            "decode_step_us": round(step_us, 2),
+            "decode_attn_GBps": round(bytes_step / step_us / 1e3, 1),
+            "note": "GB/s over the valid slots only (per-request valid counts)"}
+
+
 def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_s):
     """The same decode over a cache that keeps the whole prompt (C = L: the
     recent window widened to L - L_sink - K, so the prompt is stored as it is
@@ -429,6 +480,7 @@ def main():
     if not args.no_extras:
         res["given_lse"] = given_lse_prefill(ss, torch, w, cfg, inp)
         res["varlen_admission"] = varlen_admission(ss, torch, synth, w, cfg)
+        res["continuous_batching_decode"] = continuous_batching_decode(ss, torch, synth)
     if not (args.no_uncompressed or args.no_extras):
         caches.clear()                      # frees the compressed copies
         res["uncompressed_baseline"] = uncompressed_baseline(

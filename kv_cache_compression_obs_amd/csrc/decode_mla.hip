@@ -54,7 +54,11 @@ decode_mla_kernel(DecodeArgs a) {
   __shared__ int sh_ticket;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.y, b = blockIdx.z;
+  // split order rotated per (row, kv-head): workgroup ids fall on the XCDs
+  // round-robin, so without it one XCD would hold split 0 of every row
+  // (work that short rows keep) and another only the last splits
+  const int split = (static_cast<int>(blockIdx.x) + h + b) % a.n_split;
   const int G = a.G;
   // pos as a vector load: waiting for it does not wait for the loads after it
   const int pv = __hip_atomic_load(a.pos + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
