@@ -191,13 +191,17 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
 
   const float sc = a.scale_log2;
   const float lazy_raw = LAZY / sc;  // LAZY in raw dot-product units
-  float m[RB][4], s[RB][4], thr[RB][4];
+  // the row sums accumulate one fp32 tile sum (NKB terms) per tile in fp64:
+  // a chunk can hold thousands of keys per lane, too many for an fp32 sum to
+  // stay within the 1e-6 selection band
+  float m[RB][4], thr[RB][4];
+  double s[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       m[rb][r] = EMPTY;
-      s[rb][r] = 0.f;
+      s[rb][r] = 0.0;
       thr[rb][r] = -INFINITY;  // the first visible key raises m
     }
   // keys of a tile wholly below this bound are visible to every row and real
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
             const float tm = tile_max(rb, r);
             if (tm > thr[rb][r]) {
               const float mn = tm * sc;
-              s[rb][r] *= fast_exp2(m[rb][r] - mn);
+              s[rb][r] *= static_cast<double>(fast_exp2(m[rb][r] - mn));
               m[rb][r] = mn;
               thr[rb][r] = tm + lazy_raw;
             }
@@ -274,10 +278,13 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r) {
+          float add = 0.f;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            s[rb][r] += fast_exp2(__builtin_fmaf(acc[rb][kb][r], sc, -m[rb][r]));
+            add += fast_exp2(__builtin_fmaf(acc[rb][kb][r], sc, -m[rb][r]));
+          s[rb][r] += static_cast<double>(add);
+        }
     }
   }
   Ring::drain();
@@ -291,17 +298,17 @@ __global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) 
       M = xor_max(M, 2);
       M = xor_max(M, 4);
       M = xor_max(M, 8);
-      float sv = s[rb][r] * fast_exp2(m[rb][r] - M);
-      sv = xor_sum(sv, 1);
-      sv = xor_sum(sv, 2);
-      sv = xor_sum(sv, 4);
-      sv = xor_sum(sv, 8);
+      double sv = s[rb][r] * static_cast<double>(fast_exp2(m[rb][r] - M));
+      sv += __shfl_xor(sv, 1, WAVE);
+      sv += __shfl_xor(sv, 2, WAVE);
+      sv += __shfl_xor(sv, 4, WAVE);
+      sv += __shfl_xor(sv, 8, WAVE);
       const int row = 16 * (RB * wave + rb) + 4 * qg + r;
       if (col == 0 && row < a.Rg) {
         const size_t idx =
             ((static_cast<size_t>(bi) * a.Hkv + h) * a.Rg + row) * a.n_chunk1 + chunk;
         a.part1[2 * idx] = M == EMPTY ? -INFINITY : M;
-        a.part1[2 * idx + 1] = sv;
+        a.part1[2 * idx + 1] = static_cast<float>(sv);
       }
     }
 }
