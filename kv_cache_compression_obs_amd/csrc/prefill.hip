@@ -163,8 +163,14 @@ __device__ __forceinline__ void load_q(typename Mma<T>::frag (&qf)[D / Mma<T>::K
 // merged at the end.  m is raised only when a tile's maximum exceeds it by
 // more than 2^LAZY, so the terms stay below 2^LAZY and the rescale (one exp2
 // per row) is skipped by the whole wave on most tiles.
+//
+// The bf16 single-block shape is held to 80 VGPRs (6 waves per SIMD, 3
+// workgroups of 8 waves per CU); it fits without spilling, and one register
+// more costs a workgroup per CU (6% at 131072 keys).
 template <typename T, int D, int KT, int NWV, int NBUF, int RB>
-__global__ __launch_bounds__(64 * NWV) void score_rowstat_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * NWV)
+__attribute__((amdgpu_waves_per_eu(RB == 1 && sizeof(T) == 2 ? 6 : 1)))
+void score_rowstat_kernel(PrefillArgs a) {
   using MM = Mma<T>;
   using Ring = KeyRing<T, D, KT, NWV, NBUF>;
   constexpr int NC = D / MM::KSTEP;
