@@ -132,6 +132,12 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   if (tid * 16 < VROW)
     vld = *reinterpret_cast<const u32x4_t*>(
         reinterpret_cast<const char*>(static_cast<const T*>(a.v_new) + gh * DV) + tid * 16);
+  // this thread's rotary frequency and the row's token count (for the
+  // consistency check) are loaded here too: a load issued after the tile
+  // could only be waited for by waiting for the whole tile
+  static_assert(D / 2 <= NT, "one rotary pair per thread");
+  const double fq = tid < half ? a.inv_freq[tid] : 0.0;
+  const int ntok = tid == 0 && h == 0 && a.err != nullptr ? a.n_tokens[b] : 0;
 
   const int p = __builtin_amdgcn_readfirstlane(pv);
   if (p < 0) {  // inactive row: output 0, no state change
@@ -165,12 +171,12 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   }
   if (tid * 16 < KROW) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(kraw) + tid * 16) = kld;
   if (tid * 16 < VROW) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(vnew) + tid * 16) = vld;
-  for (int i = tid; i < half; i += NT) {
-    const double ang = static_cast<double>(p) * a.inv_freq[i];
+  if (tid < half) {
+    const double ang = static_cast<double>(p) * fq;
     double sv, cv;
     sincos(ang, &sv, &cv);
-    csn[i] = cv;
-    csn[half + i] = sv;
+    csn[tid] = cv;
+    csn[half + tid] = sv;
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += NT) {
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
     if (tid == 0) {
       a.slot_pos[gh * a.C + slot] = p;
       if (h == 0) {
-        if (a.err != nullptr && a.n_tokens[b] != p) atomicOr(a.err, 1);
+        if (a.err != nullptr && ntok != p) atomicOr(a.err, 1);
         a.n_tokens[b] = p + 1;
       }
     }

@@ -116,6 +116,11 @@ decode_mla_kernel(DecodeArgs a) {
   // reread its last chunk)
   const u32x4_t kld = *reinterpret_cast<const u32x4_t*>(static_cast<const bf16_t*>(a.k_new) +
                                                          gh * MD + 8 * min(tid, MCH - 1));
+  // this thread's first rotary frequency and the row's token count (for the
+  // consistency check) are loaded here too: a load issued after the tile
+  // could only be waited for by waiting for the whole tile
+  const double fq = tid < half ? a.inv_freq[tid] : 0.0;
+  const int ntok = tid == 0 && h == 0 && a.err != nullptr ? a.n_tokens[b] : 0;
 
   const int p = __builtin_amdgcn_readfirstlane(pv);
   if (p < 0) {  // inactive row: output 0, no state change
@@ -134,7 +139,16 @@ decode_mla_kernel(DecodeArgs a) {
   const int slot = p < SK ? p : SK + (p - SK) % a.R;
   const bool own = slot >= s0 && slot < s1;
   if (tid < MCH) reinterpret_cast<u32x4_t*>(kraw)[tid] = kld;
-  for (int i = tid; i < half; i += MNT) {
+  if (tid < half) {
+    const double ang = static_cast<double>(p) * fq;
+    double sv, cv;
+    sincos(ang, &sv, &cv);
+    csn[tid] = cv;
+    csn[half + tid] = sv;
+  }
+  // rotary ranges wider than 2*MNT dims: the remaining pairs (their
+  // frequencies are loaded late, so this path waits for the tile)
+  for (int i = tid + MNT; i < half; i += MNT) {
     const double ang = static_cast<double>(p) * a.inv_freq[i];
     double sv, cv;
     sincos(ang, &sv, &cv);
@@ -153,7 +167,7 @@ decode_mla_kernel(DecodeArgs a) {
     if (tid == 0) {
       a.slot_pos[gh * a.C + slot] = p;
       if (h == 0) {
-        if (a.err != nullptr && a.n_tokens[b] != p) atomicOr(a.err, 1);
+        if (a.err != nullptr && ntok != p) atomicOr(a.err, 1);
         a.n_tokens[b] = p + 1;
       }
     }
