@@ -308,7 +308,6 @@ ss_status decode_impl(const ss_config* cfg, const void* q, const void* k_new, co
   a.R = cfg->L_recent;
   a.split = p.split;
   a.n_split = p.n_split;
-  a.wsplit = p.wsplit;
   a.scale_log2 = scale_log2(cfg);
   a.rope_begin = cfg->rope_begin;
   a.rope_half = cfg->rope_theta > 0.f ? (cfg->rope_end - cfg->rope_begin) / 2 : 0;

@@ -18,8 +18,10 @@ using namespace dec;
 constexpr int DW = DECODE_WAVES;  // waves per decode workgroup
 
 
-// One workgroup of DW waves per (split of the slots, kv-head, row); wave w
-// streams the w-th quarter of the split.
+// One workgroup of DW waves per (split of the slots, kv-head, row).  The
+// split's 32-slot tiles go to its waves round-robin (wave w: tiles w,
+// w + DW, ...), so the waves of a workgroup read one compact window of K and
+// of V at a time.
 //
 // Prologue (whole workgroup): rotate the G queries of the kv-head at pos (fp64
 // angles) into LDS; the workgroup whose split holds the ring slot of pos also
@@ -152,13 +154,13 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   if (split >= ns) return;
   const int s0 = split * a.split;
   const int s1 = min(s0 + a.split, n_valid);
-  const int w0 = min(s0 + wave * a.wsplit, s1);  // this wave's slots [w0, w1)
-  const int w1 = min(w0 + a.wsplit, s1);
+  const int w0 = s0 + wave * TS;  // this wave's tiles start at w0, w0 + DW*TS, ... below s1
+  const int w1 = s1;              // valid slots of the split end here (rows past it clamp)
   if (w0 < w1) load_tile(w0, w1);  // the first tile, in flight during the rotary work
   const int SK = a.S + a.K;
   const int slot = p < SK ? p : SK + (p - SK) % a.R;
   const bool own = slot >= s0 && slot < s1;
-  const bool wown = slot >= w0 && slot < w1;
+  const bool wown = own && ((slot - s0) / TS) % DW == wave;
   // raw query / k_new rows into LDS behind the rotated-query area (all of it
   // is V tile space again once the main loop starts); v_new straight to vnew
   float* qs = reinterpret_cast<float*>(vt_all);                  // [G, D] rotated, fp32
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t0 = w0; t0 < w1; t0 += TS) {
+  for (int t0 = w0; t0 < w1; t0 += DW * TS) {
     wave_sync();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
           for (int i = lane; i < VROW / 4; i += 64)
             reinterpret_cast<uint32_t*>(vt + r * LROW)[i] = reinterpret_cast<const uint32_t*>(vnew)[i];
     }
-    if (t0 + TS < w1) load_tile(t0 + TS, w1);  // next tile in flight during this one
+    if (t0 + DW * TS < w1) load_tile(t0 + DW * TS, w1);  // next tile in flight during this one
 
     f32x4_t sacc[2];
 #pragma unroll

@@ -25,7 +25,6 @@ struct DecodeArgs {
   int32_t* counter;      // ws: [B, Hkv] finished-split counters, zero between calls
   int B, Hq, Hkv, G, C, S, K, R;
   int split, n_split;    // slots per workgroup split, number of splits
-  int wsplit;            // slots per wave (multiple of 32); split = DECODE_WAVES * wsplit
   float scale_log2;      // softmax scale * log2(e)
   int rope_begin;        // rotated dims [rope_begin, rope_begin + 2*rope_half)
   int rope_half;         // rotation pairs; 0: no rotation
@@ -133,7 +132,7 @@ constexpr int SCORE_WG_OVERHEAD_KEYS = 128;
 #endif
 constexpr int SCORE_NBUF = SS_SCORE_NBUF;
 // Score key tiles in LDS: 1 = XOR-permuted bf16 rows of 128 or 256 bytes,
-// 0 = rows padded by 16 bytes (affine fragment addresses).
+// 0 = padded rows (affine fragment addresses; see KeyRing::pitch).
 #ifndef SS_SCORE_SWIZZLE
 #define SS_SCORE_SWIZZLE 1
 #endif
