@@ -127,17 +127,27 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(PrefillArgs a) {
     atomicAdd(&hist[b >> 20], 1u);
   };
   if (p <= PMAX) {
+    // a chunk's staged scores (at most CH + 2*PMAX) arrive in one round of SL
+    // loads per thread, and the next chunk's round is issued before this
+    // chunk is pooled (131072-token prompts: 88 -> 78 us for this phase)
+    constexpr int SL = cdiv(CH + 2 * PMAX, NT);
+    float nx[SL];
+    auto stage_load = [&](int c0) __attribute__((always_inline)) {
+      const int s0 = max(0, c0 - p), s1 = min(m, c0 + CH + p);
+#pragma unroll
+      for (int u = 0; u < SL; ++u) {
+        const int i = s0 + tid + u * NT;
+        nx[u] = i < s1 ? raw[i] : 0.f;
+      }
+    };
+    stage_load(0);
     for (int c0 = 0; c0 < m; c0 += CH) {
       const int s0 = max(0, c0 - p), s1 = min(m, c0 + CH + p);  // staged raw[s0, s1)
       __syncthreads();  // the previous chunk's reads of stage are done (and hist is clear)
-      for (int i0 = s0 + tid; i0 < s1; i0 += UNR * NT) {  // UNR loads in flight
-        float v[UNR];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) v[u] = i0 + u * NT < s1 ? raw[i0 + u * NT] : 0.f;
-#pragma unroll
-        for (int u = 0; u < UNR; ++u)
-          if (i0 + u * NT < s1) stage[i0 + u * NT - s0] = v[u];
-      }
+      for (int u = 0; u < SL; ++u)
+        if (s0 + tid + u * NT < s1) stage[tid + u * NT] = nx[u];
+      if (c0 + CH < m) stage_load(c0 + CH);
       __syncthreads();
       for (int i = c0 + tid; i < min(m, c0 + CH); i += NT) {
         const int lo = max(0, i - p), hi = min(m - 1, i + p);

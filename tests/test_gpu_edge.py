@@ -50,3 +50,25 @@ def test_edge_decode(case):
     steps = w["L_recent"] + 40  # every ring slot rewritten at least once
     say(f"decode edge {case} C={w['C']} L={L} steps={steps}")
     decode_case(w, L=L, steps=steps, seed=62, check_every=max(1, steps // 25))
+
+
+def test_edge_prefill_all_ties_multi_chunk():
+    # zero observation queries: every visible key gets the same probability
+    # in every row, so every middle score (and every pooled score) is equal
+    # and the selection must be the K lowest middle indices.  39472 middle
+    # keys: the select kernel pools them in three LDS-staged chunks (halos at
+    # the chunk seams) and re-reads the pooled scores from memory for its
+    # radix passes and the compaction.
+    import numpy as np
+    from parity import check_prefill_group, run_lib_prefill
+    w = synth.workload(SMALL, B=1, n_q_heads=8, n_kv_heads=2, L_sink=16, K=3000, L_recent=512)
+    L = 40000
+    say(f"prefill all ties L={L} m={L - 16 - 512}")
+    inp = synth.prefill_inputs(w, 63, device="cuda", L=L)
+    inp["q_obs"].zero_()
+    res = run_lib_prefill(w, inp)
+    cache, raw, pooled, sel = res
+    for h in range(2):
+        assert (sel[0, h] == np.arange(3000)).all()
+        assert np.all(pooled[0, h] == pooled[0, h, 0])
+        check_prefill_group(w, inp, res, 0, h)
