@@ -62,8 +62,9 @@ float scale_log2(const ss_config* c) {
 // ---------------------------------------------------------------- prefill
 struct PrefillPlan {
   bool compressed;
-  int m, Rg, chunk1, n_chunk1, chunk2, n_chunk2;
-  size_t off_part1, off_rowstat, off_raw, off_pooled, off_sel, total;
+  int m, Rg, chunk1, n_chunk1, chunk2, n_chunk2, n_part, part_len;
+  size_t off_part1, off_rowstat, off_raw, off_pooled, off_sel, off_shist, off_sstate, off_scnt,
+      total;
 };
 
 PrefillPlan plan_prefill(const ss_config* c, int b, int L) {
@@ -99,6 +100,26 @@ PrefillPlan plan_prefill(const ss_config* c, int b, int L) {
   off += align_up(groups * p.m * sizeof(float));
   p.off_sel = off;
   off += align_up(groups * (c->K > 0 ? c->K : 1) * sizeof(int32_t));
+  // select: groups longer than SEL_KEEP middle keys are split into parts so
+  // that the grid has about SEL_TARGET_WG workgroups
+  p.n_part = 1;
+  p.part_len = (p.m + 63) / 64 * 64;
+  if (p.m > ss::SEL_KEEP) {
+    const long long want = (ss::SEL_TARGET_WG + static_cast<long long>(groups) - 1) /
+                           static_cast<long long>(groups);
+    const long long most = (p.m + ss::SEL_MIN_PART - 1) / ss::SEL_MIN_PART;
+    const long long parts = want < most ? want : most;
+    if (parts > 1) {
+      p.part_len = static_cast<int>((p.m + parts - 1) / parts + 63) / 64 * 64;
+      p.n_part = (p.m + p.part_len - 1) / p.part_len;
+    }
+  }
+  p.off_shist = off;
+  off += align_up(groups * p.n_part * ss::SEL_HIST_BINS * sizeof(uint32_t));
+  p.off_sstate = off;
+  off += align_up(groups * 6 * sizeof(uint32_t));
+  p.off_scnt = off;
+  off += align_up(groups * p.n_part * 2 * sizeof(uint32_t));
   p.total = off;
   return p;
 }
@@ -253,6 +274,11 @@ ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, c
     a.raw = raw_out ? raw_out : reinterpret_cast<float*>(w + p.off_raw);
     a.pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(w + p.off_pooled);
     a.sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + p.off_sel);
+    a.n_part = p.n_part;
+    a.part_len = p.part_len;
+    a.sel_hist = reinterpret_cast<uint32_t*>(w + p.off_shist);
+    a.sel_state = reinterpret_cast<uint32_t*>(w + p.off_sstate);
+    a.sel_cnt = reinterpret_cast<uint32_t*>(w + p.off_scnt);
     if (ss::launch_prefill_scores(cfg->dtype, cfg->d_qk, a, stream, ev0, ev1) != hipSuccess)
       return SS_ERR_HIP;
     if (ss::launch_prefill_select(a, stream) != hipSuccess) return SS_ERR_HIP;

@@ -52,6 +52,14 @@ struct PrefillArgs {
   int chunk1, n_chunk1;  // keys per row-stat workgroup, count
   int chunk2, n_chunk2;  // middle keys per column-score workgroup, count
   float scale_log2;
+  // select split over several workgroups per group (n_part > 1): parts of
+  // part_len middle keys (a multiple of 64), per-part digit histograms
+  // [b, Hkv, n_part, SEL_HIST_BINS], the radix state after each digit
+  // [b, Hkv, 3, 2] and per-part (greater, equal) counts [b, Hkv, n_part, 2]
+  int n_part, part_len;
+  uint32_t* sel_hist;
+  uint32_t* sel_state;
+  uint32_t* sel_cnt;
 };
 
 // The prompt of request bi: its length and the row of k (and of v) that
@@ -138,6 +146,13 @@ constexpr int SCORE_NBUF = SS_SCORE_NBUF;
 #endif
 constexpr bool SCORE_SWIZZLE = SS_SCORE_SWIZZLE != 0;
 constexpr int SCORE_LDS_BUDGET = 156 * 1024;
+// Select: a group's pooled scores stay in LDS (one workgroup) up to this many
+// middle keys; longer groups are split over several workgroups, of at least
+// SEL_MIN_PART keys each, aiming at SEL_TARGET_WG workgroups in all.
+constexpr int SEL_KEEP = 16384;
+constexpr int SEL_MIN_PART = 4096;
+constexpr int SEL_TARGET_WG = 256;
+constexpr int SEL_HIST_BINS = 2048 + 2048 + 512;  // the three radix digits
 
 // Workgroups of score pass 1 / pass 2 that run at once on the current
 // device (compute units x resident workgroups per unit) for this dtype, head
