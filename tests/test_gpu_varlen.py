@@ -77,3 +77,12 @@ def test_varlen_request_longer_than_bound_is_stored_empty():
     # max_L = 400 but request 1 has 512 tokens: that row is left empty, the
     # others are built as usual
     _varlen_case(synth.workload("tiny_fp32"), 54, [300, 512, 150], max_L=400)
+
+
+def test_varlen_long_requests_split_select():
+    # the longest request has 19472 middle keys, past the select kernel's
+    # one-workgroup limit (16384): every group is selected in parts of 3904
+    # keys (5 parts), so the 5000-token request has empty parts and the
+    # 700-token one (C = 728) is stored as it is
+    w = synth.workload("llama8b_c4k", L_sink=16, K=200, L_recent=512)
+    _varlen_case(w, 55, [20000, 700, 5000, 18000])
