@@ -126,7 +126,7 @@ PrefillPlan plan_prefill(const ss_config* c, int b, int L) {
 
 // ----------------------------------------------------------------- decode
 struct DecodePlan {
-  int split, n_split, wsplit;
+  int split, n_split;
   size_t off_cnt, n_cnt, off_o, off_ml, total;
 };
 
@@ -134,10 +134,11 @@ DecodePlan plan_decode(const ss_config* c, int B_max) {
   DecodePlan p{};
   const int C = cache_slots(c);
   const long long groups = static_cast<long long>(B_max) * c->n_kv_heads;
-  // Each workgroup of DECODE_WAVES waves takes a split of the C slots, each
-  // wave 1 to DECODE_MAX_TILES tiles of 32 slots, so that the grid holds
-  // about DECODE_TARGET_WAVES waves when every slot is valid (short splits
-  // balance rows of very different valid lengths).
+  // Each workgroup of DECODE_WAVES waves takes a split of the C slots, dealt
+  // to its waves round-robin in tiles of 32 slots, 1 to DECODE_MAX_TILES per
+  // wave, so that the grid holds about DECODE_TARGET_WAVES waves when every
+  // slot is valid (short splits balance rows of very different valid
+  // lengths).
   const long long tiles = (C + ss::DECODE_TILE - 1) / ss::DECODE_TILE;
   if (c->v_aliases_k) {
     // latent (MLA) kernel: the 4 waves of a workgroup share each tile
@@ -145,15 +146,14 @@ DecodePlan plan_decode(const ss_config* c, int B_max) {
     long long tpg = (tiles + want_wg - 1) / want_wg;
     if (tpg > ss::MLA_MAX_TILES) tpg = ss::MLA_MAX_TILES;
     if (tpg < 1) tpg = 1;
-    p.split = p.wsplit = static_cast<int>(tpg) * ss::DECODE_TILE;
+    p.split = static_cast<int>(tpg) * ss::DECODE_TILE;
   } else {
     long long want = (ss::DECODE_TARGET_WAVES + groups - 1) / groups;  // waves per group
     if (want < 1) want = 1;
     long long tpw = (tiles + want - 1) / want;
     if (tpw > ss::DECODE_MAX_TILES) tpw = ss::DECODE_MAX_TILES;
     if (tpw < 1) tpw = 1;
-    p.wsplit = static_cast<int>(tpw) * ss::DECODE_TILE;
-    p.split = ss::DECODE_WAVES * p.wsplit;
+    p.split = ss::DECODE_WAVES * static_cast<int>(tpw) * ss::DECODE_TILE;
   }
   p.n_split = (C + p.split - 1) / p.split;
   const size_t rows_q = static_cast<size_t>(B_max) * c->n_q_heads;
