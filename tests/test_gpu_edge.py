@@ -4,9 +4,11 @@ one-query observation window (W = 1), plain multi-head attention (G = 1), the
 largest group the score kernels take (G = 16, G*W = 256 rows), rotary
 embedding over part of the head (decode rotates dims 32..95 of 128) or over
 every dim of an fp32 head, and pooling windows at and past the select
-kernel's LDS staging limit or wider than the whole middle region.  Each configuration runs the prefill comparison
-(scores, selection, slot map, gathered rows) and a decode run across the ring
-wrap (outputs, written rows, n_tokens) against the oracle."""
+kernel's LDS staging limit (also on a group long enough for the select to be
+split over several workgroups) or wider than the whole middle region.  Each
+configuration runs the prefill comparison (scores, selection, slot map,
+gathered rows) and a decode run across the ring wrap (outputs, written rows,
+n_tokens) against the oracle."""
 import pytest
 
 from kv_cache_compression_obs_amd import synth
@@ -34,6 +36,10 @@ CASES = {
     "pool_513_staged_limit": (SMALL, dict(B=2, pool=513, L_sink=16, K=200, L_recent=512), 3000),
     "pool_515_unstaged": (SMALL, dict(B=2, pool=515, L_sink=16, K=200, L_recent=512), 3000),
     "pool_wider_than_middle": (TINY, dict(pool=801), 512),
+    # 39472 middle keys: the select work is split over parts of the group,
+    # and the 515-wide window is pooled straight from the raw scores
+    "pool_515_split_select": (SMALL, dict(B=1, n_q_heads=8, n_kv_heads=2, pool=515, L_sink=16,
+                                          K=3000, L_recent=512), 40000),
 }
 
 
