@@ -99,8 +99,10 @@ def measured_traffic(workload):
     return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
-def cpu_baseline(w, inp, dec, budget_s=12.0):
-    """The oracle, untuned, on a bounded sample of the same workload."""
+def cpu_baseline(w, inp, dec, budget_s=15.0):
+    """The oracle, untuned, on a bounded sample of the same workload: up to
+    half the budget of prefill compressions, then decode steps over those
+    rows for the rest of it."""
     import numpy as np
 
     import oracle
@@ -133,7 +135,7 @@ def cpu_baseline(w, inp, dec, budget_s=12.0):
         state.admit(i, r)
     t1 = time.perf_counter()
     n_dec = 0
-    while n_dec < dec["q"].shape[0] and (time.perf_counter() - t1) < budget_s / 2:
+    while n_dec < dec["q"].shape[0] and (time.perf_counter() - t1) < budget_s - t_pre:
         sl = slice(0, n_req)
         oracle.decode_step(state, synth.to_f64(dec["q"][n_dec][sl]),
                            synth.to_f64(dec["k_new"][n_dec][sl]),
