@@ -71,11 +71,12 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   __shared__ int sh_ticket;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.y, b = blockIdx.z;
-  // split order rotated per (row, kv-head): workgroup ids fall on the XCDs
-  // round-robin, so without it one XCD would hold split 0 of every row
-  // (work that short rows keep) and another only the last splits
-  const int split = (static_cast<int>(blockIdx.x) + h + b) % a.n_split;
+  // Grid (kv-head, row, split), split slowest.  Workgroup ids fall on the
+  // XCDs round-robin, so each XCD holds whole kv-heads of every row (work
+  // that short rows keep spreads over all XCDs), and when the grid fills the
+  // device twice over, the two workgroups that share a CU are splits of the
+  // same (row, kv-head).
+  const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int G = a.G;
   // pos as a vector load: waiting for it does not wait for the loads after it
   const int pv = __hip_atomic_load(a.pos + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* c, int n) {
 template <typename T, int D, int DV>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
-  decode_kernel<T, D, DV><<<dim3(a.n_split, a.Hkv, a.B), 64 * DW, 0, st>>>(a);
+  decode_kernel<T, D, DV><<<dim3(a.Hkv, a.B, a.n_split), 64 * DW, 0, st>>>(a);
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }
