@@ -54,11 +54,10 @@ decode_mla_kernel(DecodeArgs a) {
   __shared__ int sh_ticket;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.y, b = blockIdx.z;
-  // split order rotated per (row, kv-head): workgroup ids fall on the XCDs
-  // round-robin, so without it one XCD would hold split 0 of every row
-  // (work that short rows keep) and another only the last splits
-  const int split = (static_cast<int>(blockIdx.x) + h + b) % a.n_split;
+  // Grid (latent head, row, split), split slowest, as in decode_kernel:
+  // workgroup ids fall on the XCDs round-robin, so each XCD holds whole rows
+  // (work that short rows keep spreads over all XCDs)
+  const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int G = a.G;
   // pos as a vector load: waiting for it does not wait for the loads after it
   const int pv = __hip_atomic_load(a.pos + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -300,7 +299,7 @@ hipError_t launch_decode_mla(int dtype, int D, int DV, const DecodeArgs& a, hipS
                              hipEvent_t ev0, hipEvent_t ev1) {
   if (dtype != 1 || D != MD || DV != MDV) return hipErrorInvalidValue;
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
-  decode_mla_kernel<<<dim3(a.n_split, a.Hkv, a.B), MNT, 0, st>>>(a);
+  decode_mla_kernel<<<dim3(a.Hkv, a.B, a.n_split), MNT, 0, st>>>(a);
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }
