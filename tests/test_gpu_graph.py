@@ -3,7 +3,9 @@ allocation, no memset, no host synchronisation), so they can be captured into
 a HIP graph.  Each test captures the calls once, then replays the graph three
 times; between replays the program does its own eager work (restoring the
 cache, poisoning the outputs) and synchronises, and every replay must match
-the eager run bit for bit (the kernels are deterministic)."""
+the eager run bit for bit (the kernels are deterministic).  The library keeps
+no global state either: decode on two streams at once, each with its own
+workspace, gives the sequential results."""
 import pytest
 import torch
 
@@ -97,3 +99,52 @@ def test_prefill_replays_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(sel, ref_sel), f"replay {rep}"
         _same_cache(cache, ref)
+
+
+def test_decode_on_two_streams_with_separate_workspaces():
+    # the library keeps no global state: two streams (default priority)
+    # decoding different caches with their own workspaces at the same time
+    # give the sequential results
+    w = synth.workload("llama8b_c4k", **W)
+    cfg = lib_config(w)
+    B, L, T = w["B"], 2000, 8
+    say(f"two streams: {T} steps each, B={B}")
+    caches, decs, wss, errs = [], [], [], []
+    for i in range(2):
+        inp = synth.prefill_inputs(w, 80 + i, device="cuda", L=L)
+        c = ss.Cache(cfg, B)
+        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], c)
+        caches.append(c)
+        decs.append(synth.decode_inputs(w, 90 + i, T, device="cuda"))
+        wss.append(ss.decode_workspace(cfg, B))
+        errs.append(torch.zeros(1, dtype=torch.int32, device="cuda"))
+    pos = [torch.full((B,), L + t, dtype=torch.int32, device="cuda") for t in range(T)]
+    shape = (B, w["n_q_heads"], w["d_v"])
+    dt = synth.TORCH_DTYPE[w["dtype"]]
+    torch.cuda.synchronize()
+
+    def run(i, cache, out):
+        d = decs[i]
+        for t in range(T):
+            ss.ss_decode_step(cfg, d["q"][t], d["k_new"][t], d["v_new"][t], pos[t], cache, out[t],
+                              errs[i], ws=wss[i])
+
+    refs = [c.clone() for c in caches]
+    ref_out = [[torch.empty(shape, dtype=dt, device="cuda") for _ in range(T)] for _ in range(2)]
+    for i in range(2):
+        run(i, refs[i], ref_out[i])
+    torch.cuda.synchronize()
+
+    out = [[torch.empty(shape, dtype=dt, device="cuda") for _ in range(T)] for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for i, s in enumerate(streams):
+        with torch.cuda.stream(s):
+            run(i, caches[i], out[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for t in range(T):
+            assert torch.equal(out[i][t], ref_out[i][t]), f"stream {i}, step {t}"
+        _same_cache(caches[i], refs[i])
+        assert int(errs[i].item()) == 0
