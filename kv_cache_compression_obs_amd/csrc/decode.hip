@@ -89,6 +89,9 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
   frag kf[2][NC];
   u32x4_t vr[VLD];
   // Tile [t0, t0 + 32) into registers; rows at or past `hi` read row hi - 1.
+  // V rows are whole-line loads with the streaming hint; K rows keep the
+  // default policy (each K line is read in two 64-byte halves by two load
+  // instructions).
   // Always inlined: the register arrays it fills must not become stack memory.
   auto load_tile = [&](int t0, int hi) __attribute__((always_inline)) {
 #pragma unroll
@@ -102,8 +105,8 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
     for (int i = 0; i < VLD; ++i) {
       const int id = i * 64 + lane;
       const int s = min(t0 + id / VCH, hi - 1);
-      vr[i] = *reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const char*>(vb + static_cast<size_t>(s) * DV) + (id % VCH) * 16);
+      vr[i] = ld_stream(reinterpret_cast<const char*>(vb + static_cast<size_t>(s) * DV) +
+                        (id % VCH) * 16);
     }
   };
   // ---------------------------------------------------------------- loads

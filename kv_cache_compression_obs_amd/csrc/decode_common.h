@@ -47,6 +47,13 @@ __device__ __forceinline__ void st_dev4(float* p, f32x4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
+// 16-byte load of cache bytes that this launch reads once: the non-temporal
+// hint (nt) marks the lines for early eviction, so the stream does not push
+// out lines that are still in use.
+__device__ __forceinline__ u32x4_t ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 // Operands of the P.V contraction.  The contraction index of lane group qg,
 // element i is the tile-local slot 4*i + qg (i < 8), which is exactly where
 // the Q.K^T accumulator left that slot's probability (see decode_kernel).

@@ -69,14 +69,15 @@ decode_mla_kernel(DecodeArgs a) {
 
   const bf16_t* lb = static_cast<const bf16_t*>(a.kc) + gh * a.C * MD;
   u32x4_t pre[MLD];
-  // tile [t0, t0 + 32) into registers; rows at or past `hi` read row hi - 1
+  // tile [t0, t0 + 32) into registers (streaming hint); rows at or past `hi`
+  // read row hi - 1
   auto load_tile = [&](int t0, int hi) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MLD; ++i) {
       const int id = i * MNT + tid;
       const int s = min(t0 + id / MCH, hi - 1);
-      pre[i] = *reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const char*>(lb + static_cast<size_t>(s) * MD) + (id % MCH) * 16);
+      pre[i] = ld_stream(reinterpret_cast<const char*>(lb + static_cast<size_t>(s) * MD) +
+                         (id % MCH) * 16);
     }
   };
 
