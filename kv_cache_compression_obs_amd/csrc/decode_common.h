@@ -47,9 +47,8 @@ __device__ __forceinline__ void st_dev4(float* p, f32x4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
-// 16-byte load of cache bytes that this launch reads once: the non-temporal
-// hint (nt) marks the lines for early eviction, so the stream does not push
-// out lines that are still in use.
+// 16-byte load of cache bytes that this launch reads once, with the
+// non-temporal cache policy (nt: a hint that the data will not be reused).
 __device__ __forceinline__ u32x4_t ld_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
