@@ -3,9 +3,15 @@
 
 One step = one ss_prefill_compress of the whole batch (one layer) followed by
 the workload's decode steps (ss_decode_step), all inputs already resident in
-HBM.  Default workload: Llama-3.1-8B-shaped layer, bf16, 32q/8kv heads, d 128,
-batch 16, 16384-token prompts compressed to C = 4096 (64 + 1984 + 2048),
-W = 32, pool 7, RoPE 5e5, 256 decode steps.
+HBM.  Default workload: one tensor-parallel rank's share of a DeepSeek-R1 MLA
+layer in absorbed form (8 of 128 q-heads over one shared 576-dim latent whose
+first 512 dims are the value), bf16, batch 32, 131072-token prompts
+compressed to C = 32768 (64 + 960 + 31744), W = 32, pool 7, RoPE 1e4 on the
+latent's last 64 dims, 512 decode steps; the model has 61 such layers.  The
+Llama-3.1-8B-shaped layers (16384 -> 4096 at batch 16; 131072 -> 32768 at
+batch 8) are measured the same way after the timed steps and reported under
+`other_workloads`; the continuous-batching mix (64 rows, C = 32768, 1000
+decode steps with four 65536-token admissions) under `continuous_batching`.
 
 Decode runs over `--replicas` distinct copies of the layer's cache in turn
 (step t uses copy t mod replicas), so consecutive decode steps do not find
@@ -67,6 +73,32 @@ class HipEvents:
             self.lib.hipEventDestroy(e)
 
 
+def host_info():
+    """CPU model, NumPy version and the BLAS library NumPy calls."""
+    import platform
+
+    import numpy as np
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas.append(f"{p.get('internal_api')} {p.get('version')} "
+                            f"({p.get('num_threads')} threads)")
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "numpy": np.__version__, "blas": "; ".join(blas) or "unknown",
+            "host_cpus_visible": len(os.sched_getaffinity(0))}
+
+
 def algorithmic_bytes(w, elem):
     B, Hkv, d, dv, L, C = w["B"], w["n_kv_heads"], w["d_qk"], w["d_v"], w["L"], w["C"]
     row = (d + (0 if w["v_aliases_k"] else dv)) * elem
@@ -84,10 +116,18 @@ def score_flops(w):
     return 2.0 * rows * d * L, 2.0 * rows * d * (L + m)
 
 
-def measured_traffic(workload):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None if there is none for this workload or the kernel sources changed
-    since the counters were taken."""
+def score_key_bytes(w, elem):
+    """Prompt-key bytes the two score passes read (pass 1 all L keys, pass 2
+    the m middle keys)."""
+    m = w["L"] - w["L_sink"] - w["L_recent"]
+    return w["B"] * w["n_kv_heads"] * (w["L"] + m) * w["d_qk"] * elem
+
+
+def committed_profile(workload):
+    """The committed rocprofv3 record of the decode kernel on this workload
+    (HBM bytes per launch from FETCH_SIZE/WRITE_SIZE, average launch duration
+    from --kernel-trace --stats), or None if there is none or the kernel
+    sources changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
     if not os.path.exists(path):
@@ -96,7 +136,7 @@ def measured_traffic(workload):
     h = hashlib.sha256()
     for f in rec["sources"]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
-    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+    return rec if h.hexdigest() == rec["source_sha256"] else None
 
 
 def cpu_baseline(w, inp, dec, budget_s=15.0):
@@ -144,7 +184,7 @@ def cpu_baseline(w, inp, dec, budget_s=15.0):
         n_dec += 1
     t_dec = time.perf_counter() - t1
     sample_bytes = n_req * pre_b + n_dec * n_req * dec_b
-    return {
+    return dict({
         "value": sample_bytes / (t_pre + t_dec) / 1e9,
         "unit": "GB/s",
         "cores": int(cores),
@@ -154,7 +194,7 @@ def cpu_baseline(w, inp, dec, budget_s=15.0):
                    f"({t_dec:.2f} s); same algorithmic-byte accounting as value"),
         "prefill_compress_ms_per_request": 1e3 * t_pre / max(n_req, 1),
         "decode_ms_per_row_step": 1e3 * t_dec / max(n_dec * n_req, 1),
-    }
+    }, **host_info())
 
 
 def given_lse_prefill(ss, torch, w, cfg, inp, reps=5):
@@ -233,55 +273,79 @@ def varlen_admission(ss, torch, synth, w, cfg, reps=5):
     return out
 
 
-def continuous_batching_decode(ss, torch, synth, steps=64, reps=2):
-    """Decode over the continuous-batching shape (64 rows of 32q/8kv, d 128,
-    bf16, C = 32768) holding requests of log-uniform lengths in [1k, 128k]
-    (seeded): rows below capacity attend over fewer slots, so the workgroups
-    of one launch carry very different amounts of work.  The cache contents
-    are random (timing only); n_tokens holds each request's length.  Two
-    cache copies alternate, so no launch reads what the previous one left in
-    the caches."""
+def continuous_batching(ss, torch, synth, seed=5):
+    """The continuous-batching workload as specified: 64 rows of 32q/8kv,
+    d 128, bf16, C = 32768; requests of seeded log-uniform lengths in
+    [1k, 128k], each set up through ss_prefill_compress (rows at or below
+    capacity stored as they are); then 1000 decode steps, and before steps
+    200, 400, 600 and 800 a seeded row's request finishes and a new
+    65536-token prompt is compressed into that row (one single-row
+    ss_prefill_compress).  The timed region is the 1000 steps with the four
+    admissions; every input is resident beforehand."""
     w = synth.workload("llama8b_cb64")
     cfg = ss.make_config(**w)
-    B, C, Hkv, d = w["B"], w["C"], w["n_kv_heads"], w["d_qk"]
-    lens = synth.request_lengths(w, 5, B)
-    caches = [ss.Cache(cfg, B) for _ in range(2)]
-    g = torch.Generator(device="cuda").manual_seed(5)
-    for c in caches:
-        c.k.normal_(generator=g)
-        c.v.normal_(generator=g)
-    dec = synth.decode_inputs(w, 5, 8, device="cuda")
+    B, C, Hkv, d, steps = w["B"], w["C"], w["n_kv_heads"], w["d_qk"], w["steps"]
+    lens = synth.request_lengths(w, seed, B)
+    adm_rows = synth.admission_rows(w, seed)
+    cache = ss.Cache(cfg, B)
+    ws_p = torch.empty(ss.ss_prefill_workspace_bytes(cfg, 1, max(max(lens), w["L"])),
+                       dtype=torch.uint8, device="cuda")
+    for r, n in enumerate(lens):
+        inp = synth.prefill_inputs(w, seed * 1000 + r, device="cuda", B=1, L=n)
+        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], cache,
+                               rows=torch.tensor([r], dtype=torch.int32, device="cuda"), ws=ws_p)
+        del inp
+    adm = {t: (r, synth.prefill_inputs(w, seed * 1000 + 500 + t, device="cuda", B=1, L=w["L"]),
+               torch.tensor([r], dtype=torch.int32, device="cuda"))
+           for t, r in zip(w["admissions"], adm_rows)}
+    dec = synth.decode_inputs(w, seed, steps, device="cuda")
+    # positions of every step, known in advance from the schedule
+    n_tok = list(lens)
+    pos_host, valid = [], 0
+    for t in range(steps):
+        if t in adm:
+            n_tok[adm[t][0]] = w["L"]
+        pos_host.append(list(n_tok))
+        valid += sum(min(n + 1, C) for n in n_tok)
+        n_tok = [n + 1 for n in n_tok]
+    posbuf = torch.tensor(pos_host, dtype=torch.int32, device="cuda")
     out = torch.empty(B, w["n_q_heads"], d, dtype=torch.bfloat16, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = ss.decode_workspace(cfg, B)
-    pos0 = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    posbuf = [pos0 + t for t in range(steps)]
-    us = []
-    for _ in range(reps):
-        for c in caches:
-            c.n_tokens.copy_(pos0)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for t in range(steps):
-            ss.ss_decode_step(cfg, dec["q"][t % 8], dec["k_new"][t % 8], dec["v_new"][t % 8],
-                              posbuf[t // 2], caches[t % 2], out, err, ws)
-        ev[1].record()
-        torch.cuda.synchronize()
-        us.append(ev[0].elapsed_time(ev[1]) * 1e3 / steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 2 * len(adm))]
+    torch.cuda.synchronize()
+    ev[0].record()
+    k = 0
+    for t in range(steps):
+        if t in adm:
+            row, inp, rows = adm[t]
+            ev[2 + 2 * k].record()
+            ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], cache, rows=rows,
+                                   ws=ws_p)
+            ev[3 + 2 * k].record()
+            k += 1
+        ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], dec["v_new"][t], posbuf[t], cache,
+                          out, err, ws)
+    ev[1].record()
+    torch.cuda.synchronize()
     if int(err.item()) != 0:
-        raise RuntimeError("continuous-batching decode: pos != n_tokens")
-    step_us = min(us)
-    # slots attended per launch, averaged over the run (pos advances every
-    # second launch)
-    valid = sum(min(n + t // 2 + 1, C) for t in range(steps) for n in lens) / steps
-    bytes_step = valid * Hkv * 2 * d * 2
-    return {"rows": B, "cache_slots": C, "length_range": [min(lens), max(lens)],
+        raise RuntimeError("continuous batching: pos != n_tokens")
+    total_s = ev[0].elapsed_time(ev[1]) / 1e3
+    adm_s = sum(ev[2 + 2 * i].elapsed_time(ev[3 + 2 * i]) for i in range(len(adm))) / 1e3
+    dec_s = total_s - adm_s
+    bytes_dec = valid * Hkv * 2 * d * 2
+    return {"rows": B, "cache_slots": C, "decode_steps": steps,
+            "admissions": {str(t): {"row": r, "prompt": w["L"]} for t, (r, _, _) in adm.items()},
+            "length_range": [min(lens), max(lens)],
             "rows_at_capacity": sum(n >= C for n in lens),
-            "valid_slot_fraction": round(valid / (B * C), 4),
-            "decode_step_us": round(step_us, 2),
-            "decode_attn_GBps": round(bytes_step / step_us / 1e3, 1),
-            "note": "GB/s over the valid slots only (per-request valid counts)"}
+            "valid_slot_fraction": round(valid / (steps * B * C), 4),
+            "total_ms": round(1e3 * total_s, 3),
+            "admission_ms_each": round(1e3 * adm_s / max(len(adm), 1), 4),
+            "decode_step_us": round(1e6 * dec_s / steps, 2),
+            "decode_attn_GBps": round(bytes_dec / dec_s / 1e9, 1),
+            "tokens_per_s_incl_admissions": round(B * steps / total_s, 1),
+            "note": "GB/s over the valid slots only (per-request valid counts); tokens/s = "
+                    "rows x steps over the whole timed region, admissions included"}
 
 
 def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_s):
@@ -327,21 +391,149 @@ def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_s):
     }
 
 
+def run_steps(ss, torch, synth, hip, w, steps, warmup, n_dec, R, inp=None, dec=None):
+    """Build R compressed copies of the workload's cache, then run `warmup`
+    untimed and `steps` timed steps (one ss_prefill_compress of the batch +
+    n_dec ss_decode_step over the copies in turn).  The timed region is
+    bracketed by device synchronisations; per-phase times come from events
+    on the launch stream."""
+    cfg = ss.make_config(**w)
+    B, Hq, L = w["B"], w["n_q_heads"], w["L"]
+    dt = synth.TORCH_DTYPE[w["dtype"]]
+    if inp is None:
+        inp = synth.prefill_inputs(w, seed=2, device="cuda")
+    if dec is None:
+        dec = synth.decode_inputs(w, seed=2, steps=n_dec, device="cuda")
+    caches = [ss.Cache(cfg, B) for _ in range(R)]
+    ws_p = torch.empty(ss.ss_prefill_workspace_bytes(cfg, B, L), dtype=torch.uint8, device="cuda")
+    ws_d = ss.decode_workspace(cfg, B)
+    out = torch.empty(B, Hq, w["d_v"], dtype=dt, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    total_steps = warmup + steps
+    max_pos = total_steps * n_dec + 1
+    posbuf = (L + torch.arange(max_pos, dtype=torch.int32, device="cuda"))[:, None].repeat(1, B)
+    for c in caches:                       # every copy starts as a compressed prompt
+        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], c, ws=ws_p)
+    count = [0] * R
+    ev_score = [hip.create(2) for _ in range(total_steps)]
+    ev_attn = [hip.create(2) for _ in range(total_steps)]
+    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total_steps)]
+
+    def step(i):
+        e = tev[i]
+        e[0].record()
+        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], caches[0], ws=ws_p,
+                               events=(ev_score[i][0], ev_score[i][1]))
+        count[0] = 0
+        e[1].record()
+        ea = ev_attn[i]
+        for t in range(n_dec):
+            r = t % R
+            vn = dec["v_new"][t] if dec["v_new"] is not None else None
+            # one event right before the first decode kernel and one right
+            # after the last: markers between launches would perturb them
+            evs = (ea[0] if t == 0 else None, ea[1] if t == n_dec - 1 else None)
+            ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], vn, posbuf[count[r]], caches[r],
+                              out, err, ws_d, events=evs if any(evs) else None)
+            count[r] += 1
+        e[2].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, total_steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(err.item()) != 0:
+        raise RuntimeError("decode reported pos != n_tokens: the benchmark's bookkeeping is wrong")
+
+    timed = range(warmup, total_steps)
+    pre_ms = [tev[i][0].elapsed_time(tev[i][1]) for i in timed]
+    dec_ms = [tev[i][1].elapsed_time(tev[i][2]) for i in timed]
+    score_ms = [hip.elapsed_ms(ev_score[i][0], ev_score[i][1]) for i in timed]
+    attn_ms = [hip.elapsed_ms(ev_attn[i][0], ev_attn[i][1]) / n_dec for i in timed]
+    hip.destroy([e for p in ev_score for e in p] + [e for p in ev_attn for e in p])
+    elem = 2 if w["dtype"] == "bf16" else 4
+    pre_b, dec_b = algorithmic_bytes(w, elem)
+    attn_avg_s = sum(attn_ms) / len(attn_ms) / 1e3
+    dec_call_s = sum(dec_ms) / len(dec_ms) / 1e3 / n_dec
+    fl_alg, fl_exec = score_flops(w)
+    score_s = sum(score_ms) / len(score_ms) / 1e3
+    achieved = dec_b / attn_avg_s / 1e9
+    roof = {
+        "kernel": ("decode_mla_kernel" if w["v_aliases_k"] else "decode_kernel")
+        + " (RoPE + ring scatter + split-C flash-decode + merge)",
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+        "avg_launch_us": round(1e6 * attn_avg_s, 3),
+        "bytes_per_launch": dec_b,
+        "timing": "HIP events on the launch stream: one right before the first decode "
+                  "launch of a step, one right after its last; average = their distance / "
+                  "launches (includes the gaps between back-to-back launches)",
+    }
+    prof = committed_profile(w["name"])
+    if prof is not None:
+        roof["traffic"] = prof["traffic_bytes"]
+        if "rocprof_avg_us" in prof:
+            roof["rocprof_avg_us"] = prof["rocprof_avg_us"]
+            roof["frac_rocprof"] = round(dec_b / (prof["rocprof_avg_us"] * 1e-6) / 1e9
+                                         / HBM_PEAK_GBPS, 4)
+    kb = score_key_bytes(w, elem)
+    return {
+        "wall_s": wall, "step_bytes": pre_b + n_dec * dec_b, "inp": inp, "dec": dec,
+        "decode_tokens_per_s_per_layer": round(B * n_dec * steps / wall, 1),
+        "decode_tokens_per_s_model": round(B / (w["layers"] * dec_call_s), 1),
+        "decode_attn_GBps": round(dec_b / dec_call_s / 1e9, 1),
+        "decode_step_us": round(1e6 * dec_call_s, 2),
+        "prefill_compress_ms_per_layer": round(sum(pre_ms) / len(pre_ms), 4),
+        "attn_avg_s": attn_avg_s,
+        "roofline": roof,
+        "score_kernels": {
+            "avg_us": round(1e6 * score_s, 2),
+            "key_bytes": kb,
+            "hbm_GBps": round(kb / score_s / 1e9, 1),
+            "frac_hbm_peak": round(kb / score_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "tflops_algorithmic": round(fl_alg / score_s / 1e12, 2),
+            "tflops_executed": round(fl_exec / score_s / 1e12, 2),
+            "frac_bf16_peak_executed": round(fl_exec / score_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
+    }
+
+
+def describe(w, n_dec, R):
+    return (f"{w['name']}: batch {w['B']}, {w['n_q_heads']}q/{w['n_kv_heads']}kv heads, "
+            f"d {w['d_qk']}{'' if not w['v_aliases_k'] else ' latent (value = first %d)' % w['d_v']}"
+            f", prompt {w['L']} -> C={w['C']} ({w['L_sink']}+{w['K']}+{w['L_recent']}), "
+            f"W={w['W']}, pool {w['pool']}, {n_dec} decode steps, {R} cache copies, "
+            f"{w['layers']} layers in the model")
+
+
+PUBLIC_KEYS = ("decode_tokens_per_s_per_layer", "decode_tokens_per_s_model", "decode_attn_GBps",
+               "decode_step_us", "prefill_compress_ms_per_layer", "roofline", "score_kernels")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama8b_c4k")
+    ap.add_argument("--workload", default="deepseek_mla_128k")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-uncompressed", action="store_true",
                     help="skip the uncompressed-cache baseline (decode over C = L slots)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="time the step only: skip the given-lse prefill, the varlen admission "
-                         "and the uncompressed baseline (for profiling runs)")
+                    help="time the step only: skip the given-lse prefill, the varlen admission, "
+                         "the other workloads, the continuous-batching run and the "
+                         "uncompressed baseline (for profiling runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (a kernel of "
                          "known traffic, to calibrate FETCH_SIZE/WRITE_SIZE counters)")
@@ -369,128 +561,62 @@ def main():
         del src, dst
     w = synth.workload(args.workload)
     cfg = ss.make_config(**w)
-    B, Hq, L, C = w["B"], w["n_q_heads"], w["L"], w["C"]
     n_dec = args.decode_steps or w["steps"]
     R = max(1, args.replicas)
-    elem = 2 if w["dtype"] == "bf16" else 4
-    dt = synth.TORCH_DTYPE[w["dtype"]]
-
-    inp = synth.prefill_inputs(w, seed=2, device="cuda")
-    dec = synth.decode_inputs(w, seed=2, steps=n_dec, device="cuda")
-    caches = [ss.Cache(cfg, B) for _ in range(R)]
-    ws_p = torch.empty(ss.ss_prefill_workspace_bytes(cfg, B, L), dtype=torch.uint8, device="cuda")
-    ws_d = ss.decode_workspace(cfg, B)
-    out = torch.empty(B, Hq, w["d_v"], dtype=dt, device="cuda")
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    total_steps = args.warmup + args.steps
-    max_pos = total_steps * n_dec + 1
-    posbuf = (L + torch.arange(max_pos, dtype=torch.int32, device="cuda"))[:, None].repeat(1, B)
-    for c in caches:                       # every copy starts as a compressed prompt
-        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], c, ws=ws_p)
-    count = [0] * R
-
     hip = HipEvents()
-    ev_score = [hip.create(2) for _ in range(total_steps)]
-    ev_attn = [hip.create(2) for _ in range(total_steps)]
-    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total_steps)]
-
-    def step(i):
-        e = tev[i]
-        e[0].record()
-        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], caches[0], ws=ws_p,
-                               events=(ev_score[i][0], ev_score[i][1]))
-        count[0] = 0
-        e[1].record()
-        ea = ev_attn[i]
-        for t in range(n_dec):
-            r = t % R
-            vn = dec["v_new"][t] if dec["v_new"] is not None else None
-            # one event right before the first decode kernel and one right
-            # after the last: markers between launches would perturb them
-            evs = (ea[0] if t == 0 else None, ea[1] if t == n_dec - 1 else None)
-            ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], vn, posbuf[count[r]], caches[r],
-                              out, err, ws_d, events=evs if any(evs) else None)
-            count[r] += 1
-        e[2].record()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.warmup, total_steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if int(err.item()) != 0:
-        raise RuntimeError("decode reported pos != n_tokens: the benchmark's bookkeeping is wrong")
-
-    timed = range(args.warmup, total_steps)
-    pre_ms = [tev[i][0].elapsed_time(tev[i][1]) for i in timed]
-    dec_ms = [tev[i][1].elapsed_time(tev[i][2]) for i in timed]
-    score_ms = [hip.elapsed_ms(ev_score[i][0], ev_score[i][1]) for i in timed]
-    attn_ms = [hip.elapsed_ms(ev_attn[i][0], ev_attn[i][1]) / n_dec for i in timed]
-    pre_b, dec_b = algorithmic_bytes(w, elem)
-    step_b = pre_b + n_dec * dec_b
-    attn_avg_s = sum(attn_ms) / len(attn_ms) / 1e3
-    dec_call_s = sum(dec_ms) / len(dec_ms) / 1e3 / n_dec
-    fl_alg, fl_exec = score_flops(w)
-    score_s = sum(score_ms) / len(score_ms) / 1e3
-    achieved = dec_b / attn_avg_s / 1e9
-
+    r = run_steps(ss, torch, synth, hip, w, args.steps, args.warmup, n_dec, R)
+    inp, dec = r["inp"], r["dec"]
     res = {
         "metric": METRIC,
-        "value": round(step_b * args.steps / wall / 1e9, 2),
+        "value": round(r["step_bytes"] * args.steps / r["wall_s"] / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(1e3 * wall / args.steps, 4),
+        "ms_per_step": round(1e3 * r["wall_s"] / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w["dtype"],
         "data": "synthetic",
-        "config": {"workload": (f"{w['name']}: batch {B}, {Hq}q/{w['n_kv_heads']}kv heads, "
-                                f"d {w['d_qk']}, prompt {L} -> C={C} ({w['L_sink']}+{w['K']}+"
-                                f"{w['L_recent']}), W={w['W']}, pool {w['pool']}, "
-                                f"{n_dec} decode steps, {R} cache copies"),
-                   "global_batch": B, "seq_len": L, "cache_slots": C,
-                   "decode_steps_per_step": n_dec, "parallelism": "single GPU"},
-        "decode_tokens_per_s": round(B * n_dec * args.steps / wall, 1),
-        "decode_attn_GBps": round(dec_b / dec_call_s / 1e9, 1),
-        "decode_step_us": round(1e6 * dec_call_s, 2),
-        "prefill_compress_ms_per_layer": round(sum(pre_ms) / len(pre_ms), 4),
-        "roofline": {
-            "kernel": ("decode_mla_kernel" if w["v_aliases_k"] else "decode_kernel")
-            + " (RoPE + ring scatter + split-C flash-decode + merge)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(w["name"]),
-            "avg_launch_us": round(1e6 * attn_avg_s, 3),
-            "bytes_per_launch": dec_b,
-        },
-        "score_kernels": {
-            "avg_us": round(1e6 * score_s, 2),
-            "tflops_algorithmic": round(fl_alg / score_s / 1e12, 2),
-            "tflops_executed": round(fl_exec / score_s / 1e12, 2),
-            "frac_bf16_peak_executed": round(fl_exec / score_s / 1e12 / BF16_PEAK_TFLOPS, 4),
-        },
+        "config": {"workload": describe(w, n_dec, R),
+                   "global_batch": w["B"], "seq_len": w["L"], "cache_slots": w["C"],
+                   "decode_steps_per_step": n_dec, "layers_in_model": w["layers"],
+                   "parallelism": "single GPU (one tensor-parallel rank's heads)"},
+        "value_definition": "algorithmic HBM bytes of the step (prefill: prompt keys read once + "
+                            "C cache rows gathered, read and written; decode: every valid cache "
+                            "row read) per second of wall time",
     }
+    for k in PUBLIC_KEYS:
+        res[k] = r[k]
     if not args.no_extras:
         res["given_lse"] = given_lse_prefill(ss, torch, w, cfg, inp)
         res["varlen_admission"] = varlen_admission(ss, torch, synth, w, cfg)
-        res["continuous_batching_decode"] = continuous_batching_decode(ss, torch, synth)
     if not (args.no_uncompressed or args.no_extras):
-        caches.clear()                      # frees the compressed copies
+        torch.cuda.empty_cache()
         res["uncompressed_baseline"] = uncompressed_baseline(
-            ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_avg_s)
-    hip.destroy([e for p in ev_score for e in p] + [e for p in ev_attn for e in p])
+            ss, torch, hip, w, cfg, inp, dec, n_dec, R, r["attn_avg_s"])
     if not args.no_cpu_baseline:
         cpu_inp = {k: (v[:16] if v is not None else None) for k, v in inp.items()}
-        res["cpu_baseline"] = cpu_baseline(w, cpu_inp, dec)
+        cpu_dec = {k: (v.cpu() if v is not None else None) for k, v in dec.items()}
+    del r, inp, dec
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        others = {}
+        for name in ("llama8b_c4k", "llama8b_128k", "deepseek_mla_128k"):
+            if name == w["name"]:
+                continue
+            wo = synth.workload(name)
+            ro = run_steps(ss, torch, synth, hip, wo, 2, 1, wo["steps"], R)
+            others[name] = dict({"config": describe(wo, wo["steps"], R)},
+                                **{k: ro[k] for k in PUBLIC_KEYS})
+            del ro
+            torch.cuda.empty_cache()
+        res["other_workloads"] = others
+        res["continuous_batching"] = continuous_batching(ss, torch, synth)
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, cpu_inp, cpu_dec)
     print(json.dumps(res), flush=True)
 
 

@@ -120,13 +120,34 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def _check(t, name, dtype=None):
+def _check(t, name, dtype=None, shape=None):
+    """A contiguous device tensor of the given dtype and, where given, shape:
+    the kernels index every tensor by the shape the config implies, so a
+    smaller tensor would be read or written out of bounds on the device."""
     if t is None:
         return
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous device tensor")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_cache(cfg: ss_config, cache: "Cache"):
+    C = ss_cache_slots(cfg)
+    dt = TORCH_DTYPE[cfg.dtype]
+    B, H = cache.B_max, cfg.n_kv_heads
+    _check(cache.k, "cache.k", dt, (B, H, C, cfg.d_qk))
+    if cfg.v_aliases_k:
+        if cache.v is not None:
+            raise ValueError("cache.v must be None when the value aliases the key")
+    else:
+        _check(cache.v, "cache.v", dt, (B, H, C, cfg.d_v))
+        if cache.v is None:
+            raise ValueError("cache.v is required")
+    _check(cache.slot_pos, "cache.slot_pos", torch.int32, (B, H, C))
+    _check(cache.n_tokens, "cache.n_tokens", torch.int32, (B,))
 
 
 def ss_cache_slots(cfg: ss_config) -> int:
@@ -192,13 +213,30 @@ def ss_prefill_compress(cfg: ss_config, q_obs, k, v, cache: Cache, rows=None, ra
     float32 [b, n_q_heads, W] log-sum-exp of the observation rows; given, the
     call goes to ss_prefill_compress_lse (one score pass)."""
     dt = TORCH_DTYPE[cfg.dtype]
-    for t, n in ((q_obs, "q_obs"), (k, "k"), (v, "v")):
-        _check(t, n, dt)
-    _check(rows, "rows", torch.int32)
-    for t, n in ((raw_out, "raw_out"), (pooled_out, "pooled_out")):
-        _check(t, n, torch.float32)
-    _check(sel_out, "sel_out", torch.int32)
+    if k is None or k.dim() != 4:
+        raise ValueError("k must be [b, n_kv_heads, L, d_qk]")
     b, L = int(k.shape[0]), int(k.shape[2])
+    H, Hq, C = cfg.n_kv_heads, cfg.n_q_heads, ss_cache_slots(cfg)
+    m = max(L - cfg.L_sink - cfg.L_recent, 0)
+    _check(k, "k", dt, (b, H, L, cfg.d_qk))
+    if cfg.v_aliases_k:
+        if v is not None:
+            raise ValueError("v must be None when the value aliases the key")
+    else:
+        if v is None:
+            raise ValueError("v is required")
+        _check(v, "v", dt, (b, H, L, cfg.d_v))
+    if L > C or q_obs is not None:
+        if q_obs is None:
+            raise ValueError("q_obs is required when the prompt is compressed")
+        _check(q_obs, "q_obs", dt, (b, Hq, cfg.W, cfg.d_qk))
+    _check(rows, "rows", torch.int32, (b,))
+    if rows is None and b > cache.B_max:
+        raise ValueError(f"{b} requests do not fit a cache of {cache.B_max} rows")
+    for t, n in ((raw_out, "raw_out"), (pooled_out, "pooled_out")):
+        _check(t, n, torch.float32, (b, H, m))
+    _check(sel_out, "sel_out", torch.int32, (b, H, cfg.K))
+    _check_cache(cfg, cache)
     if ws is None:
         ws = torch.empty(ss_prefill_workspace_bytes(cfg, b, L), dtype=torch.uint8,
                          device=k.device)
@@ -207,7 +245,7 @@ def ss_prefill_compress(cfg: ss_config, q_obs, k, v, cache: Cache, rows=None, ra
             _ptr(ws), ws.numel(), _stream(stream))
     head = (ctypes.byref(cfg), _ptr(q_obs), _ptr(k), _ptr(v), b, L)
     if lse is not None:
-        _check(lse, "lse", torch.float32)
+        _check(lse, "lse", torch.float32, (b, Hq, cfg.W))
         args, name = head + (_ptr(lse),) + tail, "ss_prefill_compress_lse"
     else:
         args, name = head + tail, "ss_prefill_compress"
@@ -227,15 +265,29 @@ def ss_prefill_compress_varlen(cfg: ss_config, q_obs, k, v, cu_seqlens, max_L: i
     tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (int32 device [b+1]); max_L bounds
     every length.  lse: optional [b, n_q_heads, W] (one-pass scoring)."""
     dt = TORCH_DTYPE[cfg.dtype]
-    for t, n in ((q_obs, "q_obs"), (k, "k"), (v, "v")):
-        _check(t, n, dt)
-    _check(cu_seqlens, "cu_seqlens", torch.int32)
-    _check(rows, "rows", torch.int32)
-    _check(lse, "lse", torch.float32)
+    if q_obs is None or q_obs.dim() != 4 or k is None or k.dim() != 3:
+        raise ValueError("q_obs must be [b, n_q_heads, W, d_qk] and k [n_kv_heads, T, d_qk]")
+    b, T = int(q_obs.shape[0]), int(k.shape[1])
+    H, Hq = cfg.n_kv_heads, cfg.n_q_heads
+    m = max(int(max_L) - cfg.L_sink - cfg.L_recent, 0)
+    _check(q_obs, "q_obs", dt, (b, Hq, cfg.W, cfg.d_qk))
+    _check(k, "k", dt, (H, T, cfg.d_qk))
+    if cfg.v_aliases_k:
+        if v is not None:
+            raise ValueError("v must be None when the value aliases the key")
+    else:
+        if v is None:
+            raise ValueError("v is required")
+        _check(v, "v", dt, (H, T, cfg.d_v))
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (b + 1,))
+    _check(rows, "rows", torch.int32, (b,))
+    if rows is None and b > cache.B_max:
+        raise ValueError(f"{b} requests do not fit a cache of {cache.B_max} rows")
+    _check(lse, "lse", torch.float32, (b, Hq, cfg.W))
     for t, n in ((raw_out, "raw_out"), (pooled_out, "pooled_out")):
-        _check(t, n, torch.float32)
-    _check(sel_out, "sel_out", torch.int32)
-    b = int(q_obs.shape[0])
+        _check(t, n, torch.float32, (b, H, m))
+    _check(sel_out, "sel_out", torch.int32, (b, H, cfg.K))
+    _check_cache(cfg, cache)
     if ws is None:
         ws = torch.empty(ss_prefill_workspace_bytes(cfg, b, max_L), dtype=torch.uint8,
                          device=k.device)
@@ -251,16 +303,35 @@ def ss_prefill_compress_varlen(cfg: ss_config, q_obs, k, v, cu_seqlens, max_L: i
         raise SnapStreamError(st, "ss_prefill_compress_varlen")
 
 
+def _check_decode(cfg, q, k_new, v_new, pos, cache, out, err_flag):
+    dt = TORCH_DTYPE[cfg.dtype]
+    B, H, Hq = cache.B_max, cfg.n_kv_heads, cfg.n_q_heads
+    for t, n in ((q, "q"), (k_new, "k_new"), (out, "out"), (pos, "pos")):
+        if t is None:
+            raise ValueError(f"{n} is required")
+    _check(q, "q", dt, (B, Hq, cfg.d_qk))
+    _check(k_new, "k_new", dt, (B, H, cfg.d_qk))
+    if cfg.v_aliases_k:
+        if v_new is not None:
+            raise ValueError("v_new must be None when the value aliases the key")
+    else:
+        if v_new is None:
+            raise ValueError("v_new is required")
+        _check(v_new, "v_new", dt, (B, H, cfg.d_v))
+    _check(out, "out", dt, (B, Hq, cfg.d_v))
+    _check(pos, "pos", torch.int32, (B,))
+    _check(err_flag, "err_flag", torch.int32)
+    if err_flag is not None and err_flag.numel() < 1:
+        raise ValueError("err_flag must hold at least one int32")
+    _check_cache(cfg, cache)
+
+
 def ss_decode_step(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, out, err_flag=None,
                    ws=None, stream=None, events=None) -> None:
     """One decode step of every cache row; writes `out` [B_max, Hq, d_v].
     events: optional pair of raw hipEvent_t handles recorded around the
     attention kernel."""
-    dt = TORCH_DTYPE[cfg.dtype]
-    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out")):
-        _check(t, n, dt)
-    _check(pos, "pos", torch.int32)
-    _check(err_flag, "err_flag", torch.int32)
+    _check_decode(cfg, q, k_new, v_new, pos, cache, out, err_flag)
     if ws is None:
         ws = decode_workspace(cfg, cache.B_max, q.device)
     cs = cache.struct()
@@ -272,3 +343,4 @@ def ss_decode_step(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, out, err_
         st = lib().ss_decode_step_timed(*args, events[0], events[1])
     if st != SS_OK:
         raise SnapStreamError(st, "ss_decode_step")
+

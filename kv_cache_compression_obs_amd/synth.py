@@ -22,7 +22,9 @@ page's configured L_recent = 31,744):
                       per-head 128 + 64 query dims before absorption),
                       61 layers, 512 steps
   llama8b_cb64        64 rows x (32q/8kv) x d128, bf16, C=32768, request
-                      lengths log-uniform in [1k, 128k], 1000 steps
+                      lengths log-uniform in [1k, 128k], 1000 steps; before
+                      steps 200/400/600/800 a seeded row's request is replaced
+                      by a new 65536-token prompt
 """
 from __future__ import annotations
 
@@ -150,6 +152,13 @@ def request_lengths(w: dict, seed: int, n: int) -> list[int]:
     u = torch.rand(n, generator=g, dtype=torch.float64)
     lo, hi = math.log(w["len_min"]), math.log(w["len_max"])
     return [int(round(math.exp(lo + float(x) * (hi - lo)))) for x in u]
+
+
+def admission_rows(w: dict, seed: int) -> list[int]:
+    """Continuous-batching schedule: the distinct rows (seeded) whose requests
+    finish and are replaced by a new prompt, one per step of w["admissions"]."""
+    g = _gen(seed + 9_999, "cpu")
+    return torch.randperm(w["B"], generator=g)[:len(w["admissions"])].tolist()
 
 
 def to_f64(t):

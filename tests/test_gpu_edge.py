@@ -78,3 +78,32 @@ def test_edge_prefill_all_ties_multi_chunk():
         assert (sel[0, h] == np.arange(3000)).all()
         assert np.all(pooled[0, h] == pooled[0, h, 0])
         check_prefill_group(w, inp, res, 0, h)
+
+
+def test_binding_rejects_tensors_of_the_wrong_shape():
+    # the kernels index every tensor by the shape the config implies; the
+    # binding refuses a smaller tensor before anything is launched
+    import torch
+
+    from kv_cache_compression_obs_amd import snapstream as ss
+    w = synth.workload(SMALL, B=4, L_sink=16, K=200, L_recent=512)
+    cfg = ss.make_config(**w)
+    cache = ss.Cache(cfg, 4)
+    q = torch.zeros(4, 32, 128, dtype=torch.bfloat16, device="cuda")
+    kn = torch.zeros(4, 8, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(4, 32, 128, dtype=torch.bfloat16, device="cuda")
+    pos = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for bad in (dict(pos=pos[:3]), dict(q=q[:, :16].contiguous()), dict(out=out[:2]),
+                dict(kn=kn[..., :64].contiguous())):
+        a = dict(q=q, kn=kn, out=out, pos=pos)
+        a.update(bad)
+        with pytest.raises(ValueError):
+            ss.ss_decode_step(cfg, a["q"], a["kn"], a["kn"], a["pos"], cache, a["out"])
+    inp = synth.prefill_inputs(w, 5, device="cuda", B=2, L=1000)
+    with pytest.raises(ValueError):                       # window of the wrong length
+        ss.ss_prefill_compress(cfg, inp["q_obs"][:, :, :16].contiguous(), inp["k"], inp["v"], cache)
+    with pytest.raises(ValueError):                       # sel_out too short
+        ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], cache,
+                               sel_out=torch.zeros(2, 8, 10, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(cache.n_tokens.sum().item()) == 0
