@@ -57,7 +57,9 @@ typedef enum {
   SS_ERR_INVALID_ARG = 1,  /* a scalar or pointer argument is invalid; nothing was launched */
   SS_ERR_UNSUPPORTED = 2,  /* valid, but this build has no kernel for the shape/dtype */
   SS_ERR_WORKSPACE = 3,    /* ws_bytes is smaller than the matching *_workspace_bytes() */
-  SS_ERR_HIP = 4           /* a HIP launch failed (hipGetLastError after the launch) */
+  SS_ERR_HIP = 4,          /* a HIP launch failed (hipGetLastError after the launch) */
+  SS_ERR_SCRATCH_LIMIT = 5 /* ss_decode_step_noalloc: the shapes need more scratch than the
+                              library's static array holds; nothing was launched */
 } ss_status;
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
@@ -223,6 +225,29 @@ ss_status ss_decode_step(const ss_config* cfg, const void* q, const void* k_new,
                          const void* v_new, const int32_t* pos, const ss_cache* cache,
                          void* out, int32_t* err_flag, void* ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/* ss_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and single kernel as ss_decode_step, without the
+ * workspace: the split partials and completion counters live in a static
+ * device array of the library (16 MiB per GPU, held until the process ends,
+ * looked up on the first call on each device; that first call also enqueues
+ * one small kernel on `stream` that zeroes the counters).  No call allocates
+ * or frees memory.
+ *
+ * Limit: B_max * n_kv_heads <= 16384 and the partials of
+ * B_max * n_q_heads * n_split * (d_v + 2) fp32 values (n_split as
+ * ss_decode_step plans it for the cache shape) within 16 MiB - 64 KiB; larger
+ * shapes return SS_ERR_SCRATCH_LIMIT before any launch.  Every shape the
+ * workloads of this library use fits (e.g. 64 rows x 32 q-heads x 32768 slots,
+ * or 32 rows x 8 latent heads x 32768 slots: about 8.6 MB).
+ *
+ * All calls on one GPU share the array, which keeps the last call's partials:
+ * calls that overlap on one GPU (other streams, other threads, graph replays
+ * in flight) race and must be serialised by the caller. */
+ss_status ss_decode_step_noalloc(const ss_config* cfg, const void* q, const void* k_new,
+                                 const void* v_new, const int32_t* pos, const ss_cache* cache,
+                                 void* out, int32_t* err_flag, hipStream_t stream);
 
 /* Profiling variants: identical to the calls above, and additionally record
  * `begin` / `end` on `stream` immediately before and after the dominant

@@ -130,7 +130,10 @@ struct DecodePlan {
   size_t off_cnt, n_cnt, off_o, off_ml, total;
 };
 
-DecodePlan plan_decode(const ss_config* c, int B_max) {
+// cnt_region: bytes reserved for the counters at the start of the workspace
+// (at least what they need): the static scratch keeps a fixed region so that
+// its partials never overlap counters of a call of another shape.
+DecodePlan plan_decode(const ss_config* c, int B_max, size_t cnt_region = 0) {
   DecodePlan p{};
   const int C = cache_slots(c);
   const long long groups = static_cast<long long>(B_max) * c->n_kv_heads;
@@ -160,7 +163,7 @@ DecodePlan plan_decode(const ss_config* c, int B_max) {
   size_t off = 0;
   p.off_cnt = off;
   p.n_cnt = static_cast<size_t>(groups);
-  off += align_up(p.n_cnt * sizeof(int32_t));
+  off += align_up(p.n_cnt * sizeof(int32_t) > cnt_region ? p.n_cnt * sizeof(int32_t) : cnt_region);
   p.off_o = off;
   off += align_up(rows_q * p.n_split * c->d_v * sizeof(float));
   p.off_ml = off;
@@ -292,10 +295,12 @@ ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, c
   return SS_OK;
 }
 
+// use_static: the workspace is the library's static scratch (ws, ws_bytes
+// ignored).
 ss_status decode_impl(const ss_config* cfg, const void* q, const void* k_new, const void* v_new,
                       const int32_t* pos, const ss_cache* cache, void* out, int32_t* err_flag,
                       void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t ev0,
-                      hipEvent_t ev1) {
+                      hipEvent_t ev1, bool use_static = false) {
   const ss_status cs = check_config(cfg);
   if (cs != SS_OK) return cs;
   if (cache == nullptr || q == nullptr || k_new == nullptr || pos == nullptr || out == nullptr ||
@@ -304,9 +309,17 @@ ss_status decode_impl(const ss_config* cfg, const void* q, const void* k_new, co
     return SS_ERR_INVALID_ARG;
   if (!cfg->v_aliases_k && (v_new == nullptr || cache->v == nullptr)) return SS_ERR_INVALID_ARG;
   if (misaligned(q) || misaligned(k_new) || misaligned(v_new) || misaligned(cache->k) ||
-      misaligned(cache->v) || misaligned(ws))
+      misaligned(cache->v) || (!use_static && misaligned(ws)))
     return SS_ERR_INVALID_ARG;
-  const DecodePlan p = plan_decode(cfg, cache->B_max);
+  const DecodePlan p =
+      plan_decode(cfg, cache->B_max, use_static ? ss::STATIC_SCRATCH_PARTIALS_OFF : 0);
+  if (use_static) {
+    if (p.n_cnt > static_cast<size_t>(ss::STATIC_SCRATCH_COUNTERS) ||
+        p.total > ss::STATIC_SCRATCH_BYTES)
+      return SS_ERR_SCRATCH_LIMIT;
+    if (ss::static_scratch(&ws, stream) != hipSuccess) return SS_ERR_HIP;
+    ws_bytes = ss::STATIC_SCRATCH_BYTES;
+  }
   if (ws == nullptr || ws_bytes < p.total) return SS_ERR_WORKSPACE;
 
   ss::DecodeArgs a{};
@@ -427,6 +440,13 @@ ss_status ss_decode_step_timed(const ss_config* cfg, const void* q, const void* 
                      end);
 }
 
+ss_status ss_decode_step_noalloc(const ss_config* cfg, const void* q, const void* k_new,
+                                 const void* v_new, const int32_t* pos, const ss_cache* cache,
+                                 void* out, int32_t* err_flag, hipStream_t stream) {
+  return decode_impl(cfg, q, k_new, v_new, pos, cache, out, err_flag, nullptr, 0, stream, nullptr,
+                     nullptr, true);
+}
+
 const char* ss_status_string(int32_t status) {
   switch (status) {
     case SS_OK: return "ok";
@@ -434,6 +454,7 @@ const char* ss_status_string(int32_t status) {
     case SS_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case SS_ERR_WORKSPACE: return "workspace too small";
     case SS_ERR_HIP: return "HIP launch error";
+    case SS_ERR_SCRATCH_LIMIT: return "shapes need more than the static decode scratch";
     default: return "unknown status";
   }
 }

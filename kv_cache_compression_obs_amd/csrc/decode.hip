@@ -7,6 +7,8 @@
 // window: the new key/value is scattered into a fixed slot, nothing is
 // gathered or concatenated) and "Prefill / Decode Pipeline" (decode is bound
 // by the bytes of cache it reads every step).
+#include <mutex>
+
 #include "decode_common.h"
 
 namespace ss {
@@ -386,6 +388,37 @@ hipError_t launch_decode(int dtype, int D, int DV, int alias, const DecodeArgs& 
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t st) {
   zero_counters_kernel<<<cdiv(n, 256), 256, 0, st>>>(counters, n);
   return hipGetLastError();
+}
+
+// Decode scratch of ss_decode_step_noalloc.  In host code `scratch` names a
+// host-side stand-in, not device memory: host code only ever uses the device
+// address that hipGetSymbolAddress returns for the current device (each GPU
+// holds its own copy of the array).
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(void** ptr, hipStream_t st) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    // The loader zero-fills the array; the counters are cleared once more
+    // here, by a kernel on the caller's stream (also valid under capture),
+    // before the first decode that uses them.  Every decode leaves them zero.
+    e = launch_zero_counters(static_cast<int32_t*>(p), STATIC_SCRATCH_COUNTERS, st);
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace ss

@@ -87,6 +87,19 @@ hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStre
 hipError_t launch_decode_mla(int dtype, int D, int DV, const DecodeArgs& a, hipStream_t st,
                              hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t st);
+
+// The library's own decode scratch for callers that cannot allocate: a
+// device array of STATIC_SCRATCH_BYTES per GPU, held until the process ends.
+// Its first STATIC_SCRATCH_COUNTERS int32 are the completion counters (this
+// region is never used for anything else, so the counters stay zero between
+// calls whatever their shapes); the split partials follow from
+// STATIC_SCRATCH_PARTIALS_OFF.  static_scratch returns the array's device
+// address on the current device, looking it up (and zeroing the counters on
+// `st`) the first time it is asked for on that device.
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(16) << 20;
+constexpr int STATIC_SCRATCH_COUNTERS = 16384;
+constexpr size_t STATIC_SCRATCH_PARTIALS_OFF = STATIC_SCRATCH_COUNTERS * sizeof(int32_t);
+hipError_t static_scratch(void** ptr, hipStream_t st);
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_gather(int dtype, int D, int DV, int alias, bool compressed,
                                  const PrefillArgs& a, hipStream_t st);

@@ -13,7 +13,8 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsnapstream.so")
 
-SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_WORKSPACE, SS_ERR_HIP = range(5)
+(SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_WORKSPACE, SS_ERR_HIP,
+ SS_ERR_SCRATCH_LIMIT) = range(6)
 SS_F32, SS_BF16 = 0, 1
 DTYPES = {"f32": SS_F32, "bf16": SS_BF16}
 TORCH_DTYPE = {SS_F32: torch.float32, SS_BF16: torch.bfloat16}
@@ -22,7 +23,7 @@ EXPORTS = ("ss_cache_slots", "ss_prefill_workspace_bytes", "ss_decode_workspace_
            "ss_decode_workspace_init", "ss_prefill_compress", "ss_decode_step",
            "ss_prefill_compress_timed", "ss_decode_step_timed", "ss_prefill_compress_lse",
            "ss_prefill_compress_lse_timed", "ss_prefill_compress_varlen",
-           "ss_prefill_compress_varlen_timed", "ss_status_string")
+           "ss_prefill_compress_varlen_timed", "ss_decode_step_noalloc", "ss_status_string")
 
 
 class ss_config(ctypes.Structure):
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
         L.ss_prefill_compress_varlen_timed.argtypes = (L.ss_prefill_compress_varlen.argtypes +
                                                        [VP, VP])
         L.ss_prefill_compress_varlen_timed.restype = I32
+        L.ss_decode_step_noalloc.argtypes = [P(ss_config), VP, VP, VP, VP, P(ss_cache), VP, VP,
+                                             VP]
+        L.ss_decode_step_noalloc.restype = I32
         L.ss_decode_workspace_init.argtypes = [P(ss_config), I32, VP, SZ, VP]
         L.ss_decode_workspace_init.restype = I32
         L.ss_status_string.argtypes = [I32]
@@ -344,3 +348,15 @@ def ss_decode_step(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, out, err_
     if st != SS_OK:
         raise SnapStreamError(st, "ss_decode_step")
 
+
+def ss_decode_step_noalloc(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, out,
+                           err_flag=None, stream=None) -> None:
+    """ss_decode_step without a workspace: the library's static device scratch
+    holds the split partials (calls on one GPU must not overlap)."""
+    _check_decode(cfg, q, k_new, v_new, pos, cache, out, err_flag)
+    cs = cache.struct()
+    st = lib().ss_decode_step_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                      _ptr(pos), ctypes.byref(cs), _ptr(out), _ptr(err_flag),
+                                      _stream(stream))
+    if st != SS_OK:
+        raise SnapStreamError(st, "ss_decode_step_noalloc")
