@@ -79,13 +79,18 @@ PrefillPlan plan_prefill(const ss_config* c, int b, int L) {
   // chunk lengths that fill whole rounds of the current device; the
   // compile-time defaults when it cannot be queried
   int slots1 = 0, slots2 = 0;
+  // the register-query passes stage at most DIRECT_STAGE_KEYS column sums
+  // per wave in pass 2
+  const int max2 = ss::direct_scores_supported(c->dtype, c->d_qk, p.Rg)
+                       ? ss::DIRECT_WAVES * ss::DIRECT_STAGE_KEYS
+                       : 0;
   if (ss::prefill_score_slots(c->dtype, c->d_qk, p.Rg, &slots1, &slots2) == hipSuccess) {
     p.chunk1 = ss::score_chunk(L, static_cast<long long>(groups), slots1);
-    p.chunk2 = ss::score_chunk(p.m, static_cast<long long>(groups), slots2);
+    p.chunk2 = ss::score_chunk(p.m, static_cast<long long>(groups), slots2, max2);
   } else {
     (void)hipGetLastError();  // a failed query leaves no error for later calls
     p.chunk1 = ss::SCORE_CHUNK1;
-    p.chunk2 = ss::SCORE_CHUNK2;
+    p.chunk2 = max2 > 0 && ss::SCORE_CHUNK2 > max2 ? max2 : ss::SCORE_CHUNK2;
   }
   p.n_chunk1 = (L + p.chunk1 - 1) / p.chunk1;
   p.n_chunk2 = (p.m + p.chunk2 - 1) / p.chunk2;

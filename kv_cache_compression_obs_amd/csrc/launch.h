@@ -167,6 +167,38 @@ constexpr int SEL_MIN_PART = 4096;
 constexpr int SEL_TARGET_WG = 256;
 constexpr int SEL_HIST_BINS = 2048 + 2048 + 512;  // the three radix digits
 
+// Score passes with the group's query rows in registers (score.hip), for
+// groups of at most 128 rows of 64 or 128 dims: DIRECT_WAVES waves per
+// workgroup, each with a ring of DIRECT_RING1 (pass 1) / DIRECT_RING2
+// (pass 2) 16-key tiles in LDS; pass 2 stages the sums of at most
+// DIRECT_STAGE_KEYS keys per wave, which bounds its chunk at
+// DIRECT_WAVES * DIRECT_STAGE_KEYS keys.  DIRECT_CPOL: cache-policy bits of
+// the direct key loads (2: nt, non-temporal; each key is read once per pass).
+#ifndef SS_DIRECT_RING1
+#define SS_DIRECT_RING1 4
+#endif
+#ifndef SS_DIRECT_RING2
+#define SS_DIRECT_RING2 4
+#endif
+#ifndef SS_DIRECT_CPOL
+#define SS_DIRECT_CPOL 2
+#endif
+constexpr int DIRECT_WAVES = 4;
+constexpr int DIRECT_RING1 = SS_DIRECT_RING1;
+constexpr int DIRECT_RING2 = SS_DIRECT_RING2;
+constexpr int DIRECT_CPOL = SS_DIRECT_CPOL;
+#ifndef SS_DIRECT_STAGE_KEYS
+#define SS_DIRECT_STAGE_KEYS 1024
+#endif
+constexpr int DIRECT_STAGE_KEYS = SS_DIRECT_STAGE_KEYS;
+bool direct_scores_supported(int dtype, int D, int Rg);
+hipError_t launch_direct_scores(int dtype, int D, const PrefillArgs& a, hipStream_t st,
+                                hipEvent_t ev0, hipEvent_t ev1);
+hipError_t direct_score_slots(int dtype, int D, int Rg, int* slots1, int* slots2);
+// the row-statistics kernels shared by both score paths (prefill.hip)
+void launch_lse_rowstat(const PrefillArgs& a, unsigned grid, hipStream_t st);
+void launch_rowstat_combine(const PrefillArgs& a, unsigned grid, hipStream_t st);
+
 // Workgroups of score pass 1 / pass 2 that run at once on the current
 // device (compute units x resident workgroups per unit) for this dtype, head
 // size and padded group row count; hipErrorInvalidValue for a shape without
@@ -176,12 +208,15 @@ hipError_t prefill_score_slots(int dtype, int D, int Rg, int* slots1, int* slots
 // Keys per workgroup for `keys` keys in each of `groups` groups when `slots`
 // workgroups run at once: the multiple of SCORE_KT_MAX that minimises
 // rounds x (chunk + SCORE_WG_OVERHEAD_KEYS).
-inline int score_chunk(int keys, long long groups, int slots) {
+// max_chunk (> 0): no chunk longer than that many keys.
+inline int score_chunk(int keys, long long groups, int slots, int max_chunk = 0) {
   const int tiles = (keys + SCORE_KT_MAX - 1) / SCORE_KT_MAX;
-  int best = tiles * SCORE_KT_MAX;
+  const int max_ct = max_chunk > 0 ? max_chunk / SCORE_KT_MAX : tiles;
+  int best = -1;
   long long best_cost = -1;
   for (int n = 1; n <= tiles; ++n) {
     const int ct = (tiles + n - 1) / n;  // tiles per chunk
+    if (ct > max_ct) continue;
     const int n_eff = (tiles + ct - 1) / ct;
     const long long rounds = (groups * n_eff + slots - 1) / slots;
     const long long cost =
@@ -191,7 +226,7 @@ inline int score_chunk(int keys, long long groups, int slots) {
       best = ct * SCORE_KT_MAX;
     }
   }
-  return best;
+  return best > 0 ? best : max_ct * SCORE_KT_MAX;
 }
 
 }  // namespace ss

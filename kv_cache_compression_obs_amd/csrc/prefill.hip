@@ -622,6 +622,7 @@ hipError_t score_slots(int Rg, int* slots1, int* slots2) {
 }  // namespace
 
 hipError_t prefill_score_slots(int dtype, int D, int Rg, int* slots1, int* slots2) {
+  if (direct_scores_supported(dtype, D, Rg)) return direct_score_slots(dtype, D, Rg, slots1, slots2);
   if (dtype == 0 && D == 64) return score_slots<float, 64, 64>(Rg, slots1, slots2);
   if (dtype == 0 && D == 128) return score_slots<float, 128, 64>(Rg, slots1, slots2);
   if (dtype == 1 && D == 64) return score_slots<bf16_t, 64, 64>(Rg, slots1, slots2);
@@ -630,8 +631,16 @@ hipError_t prefill_score_slots(int dtype, int D, int Rg, int* slots1, int* slots
   return hipErrorInvalidValue;
 }
 
+void launch_lse_rowstat(const PrefillArgs& a, unsigned grid, hipStream_t st) {
+  lse_rowstat_kernel<<<grid, 256, 0, st>>>(a);
+}
+void launch_rowstat_combine(const PrefillArgs& a, unsigned grid, hipStream_t st) {
+  score_rowstat_combine_kernel<<<grid, 256, 0, st>>>(a);
+}
+
 hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStream_t st,
                                  hipEvent_t ev0, hipEvent_t ev1) {
+  if (direct_scores_supported(dtype, D, a.Rg)) return launch_direct_scores(dtype, D, a, st, ev0, ev1);
   if (dtype == 0 && D == 64) return run_scores<float, 64, 64>(a, st, ev0, ev1);
   if (dtype == 0 && D == 128) return run_scores<float, 128, 64>(a, st, ev0, ev1);
   if (dtype == 1 && D == 64) return run_scores<bf16_t, 64, 64>(a, st, ev0, ev1);
