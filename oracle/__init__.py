@@ -9,6 +9,8 @@ from .snapstream_oracle import (  # noqa: F401
     PrefillResult,
     attend,
     decode_step,
+    decode_write,
+    fixed_cache_layout,
     max_pool_clipped,
     obs_column_scores,
     prefill_compress_one,

@@ -241,11 +241,11 @@ def prefill_compress_one(cfg: Config, q_obs: np.ndarray, k: np.ndarray,
     S, K, R, C = cfg.L_sink, cfg.K, cfg.L_recent, cfg.C
     Hkv, L, _ = k.shape
     G = cfg.G
-    k_cache = np.zeros((Hkv, C, cfg.d_qk))
-    v_cache = None if cfg.v_aliases_k else np.zeros((Hkv, C, cfg.d_v))
-    slot_pos = np.full((Hkv, C), -1, dtype=np.int64)
 
     if L <= C:
+        k_cache = np.zeros((Hkv, C, cfg.d_qk))
+        v_cache = None if cfg.v_aliases_k else np.zeros((Hkv, C, cfg.d_v))
+        slot_pos = np.full((Hkv, C), -1, dtype=np.int64)
         for h in range(Hkv):
             k_cache[h, :L] = k[h]
             if v_cache is not None:
@@ -265,16 +265,33 @@ def prefill_compress_one(cfg: Config, q_obs: np.ndarray, k: np.ndarray,
         pooled = max_pool_clipped(raw, cfg.pool)
         sel = select_topk(pooled, K)
         cols[h], raws[h], pools[h], sels[h] = col, raw, pooled, sel
-        tokens = list(range(S)) + [S + int(j) for j in sel] + list(range(L - R, L))
+    k_cache, v_cache, slot_pos = fixed_cache_layout(cfg, k, v, sels)
+    return PrefillResult(cols, raws, pools, sels, k_cache, v_cache, slot_pos, L)
+
+
+def fixed_cache_layout(cfg: Config, k: np.ndarray, v: np.ndarray | None, sel: np.ndarray):
+    """The fixed cache of one compressed request (L > C) from its kept middle
+    tokens sel [Hkv, K] (ascending indices into the middle region): returns
+    (k_cache [Hkv, C, d_qk], v_cache [Hkv, C, d_v] or None, slot_pos [Hkv, C]).
+
+    [COMP] "Fixed-Size Cache Layout": sink tokens, then the selected middle
+    tokens, then the recent window.  READING: sinks and selected tokens take
+    slots 0 .. S+K-1 in position order; recent token t goes to its ring slot
+    ([COMP] "Ring Buffer vs. Naive Slicing")."""
+    S, K, R, C = cfg.L_sink, cfg.K, cfg.L_recent, cfg.C
+    Hkv, L, _ = k.shape
+    k_cache = np.zeros((Hkv, C, cfg.d_qk))
+    v_cache = None if cfg.v_aliases_k else np.zeros((Hkv, C, cfg.d_v))
+    slot_pos = np.full((Hkv, C), -1, dtype=np.int64)
+    for h in range(Hkv):
+        tokens = list(range(S)) + [S + int(j) for j in sel[h]] + list(range(L - R, L))
         for t_idx, t in enumerate(tokens):
-            # sinks and selected middle tokens take slots 0 .. S+K-1 in order;
-            # recent tokens go to their ring slot.
             slot = t_idx if t_idx < S + K else ring_slot(t, S, K, R)
             k_cache[h, slot] = k[h, t]
             if v_cache is not None:
                 v_cache[h, slot] = v[h, t]
             slot_pos[h, slot] = t
-    return PrefillResult(cols, raws, pools, sels, k_cache, v_cache, slot_pos, L)
+    return k_cache, v_cache, slot_pos
 
 
 # --------------------------------------------------------------------------
@@ -316,28 +333,21 @@ def attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float) -> n
     return (e / e.sum()) @ vals
 
 
-def decode_step(state: CacheState, q: np.ndarray, k_new: np.ndarray,
-                v_new: np.ndarray | None, pos: np.ndarray):
-    """One decode step for every row.
+def decode_write(state: CacheState, k_new: np.ndarray, v_new: np.ndarray | None,
+                 pos: np.ndarray) -> bool:
+    """The cache update of one decode step for every row (no attention).
 
-    q [B, Hq, d_qk], k_new [B, Hkv, d_qk] (pre-RoPE), v_new [B, Hkv, d_v] or
-    None when v aliases k, pos [B] absolute positions (< 0: inactive row).
+    k_new [B, Hkv, d_qk] (pre-RoPE), v_new [B, Hkv, d_v] or None when v
+    aliases k, pos [B] absolute positions (< 0: inactive row).
 
     [COMP] "Ring Buffer vs. Naive Slicing": the new key/value is scattered into
-    a fixed slot of the recent window (no gather, no concatenation); attention
-    then runs over every valid slot of the fixed cache ([COMP] "Prefill /
-    Decode Pipeline": decode is a memory-bound pass over the cache).
-    READING: the new token is written (evicting position pos - L_recent) before
-    attention and attends to itself; the valid slots of a row are its first
-    min(n_tokens, C) slots.  Returns (out [B, Hq, d_v], err) where err is True
-    if some active row had pos != n_tokens (the step is applied at pos anyway).
-    """
+    a fixed slot of the recent window (no gather, no concatenation), evicting
+    position pos - L_recent.  READING: RoPE at the absolute position, the
+    rotated key rounded once to the cache dtype.  Returns True if some active
+    row had pos != n_tokens (the write is applied at pos anyway)."""
     cfg = state.cfg
-    B = q.shape[0]
-    G, C = cfg.G, cfg.C
-    out = np.zeros((B, cfg.n_q_heads, cfg.d_v))
     err = False
-    for b in range(B):
+    for b in range(k_new.shape[0]):
         p = int(pos[b])
         if p < 0:
             continue
@@ -350,6 +360,32 @@ def decode_step(state: CacheState, q: np.ndarray, k_new: np.ndarray,
             state.v[b, :, slot] = v_new[b]
         state.slot_pos[b, :, slot] = p
         state.n_tokens[b] = p + 1
+    return err
+
+
+def decode_step(state: CacheState, q: np.ndarray, k_new: np.ndarray,
+                v_new: np.ndarray | None, pos: np.ndarray):
+    """One decode step for every row.
+
+    q [B, Hq, d_qk], k_new [B, Hkv, d_qk] (pre-RoPE), v_new [B, Hkv, d_v] or
+    None when v aliases k, pos [B] absolute positions (< 0: inactive row).
+
+    The cache update is decode_write; attention then runs over every valid
+    slot of the fixed cache ([COMP] "Prefill / Decode Pipeline": decode is a
+    memory-bound pass over the cache).  READING: the new token is written
+    before attention and attends to itself; the valid slots of a row are its
+    first min(n_tokens, C) slots.  Returns (out [B, Hq, d_v], err) where err is
+    True if some active row had pos != n_tokens (the step is applied at pos
+    anyway)."""
+    cfg = state.cfg
+    B = q.shape[0]
+    G, C = cfg.G, cfg.C
+    out = np.zeros((B, cfg.n_q_heads, cfg.d_v))
+    err = decode_write(state, k_new, v_new, pos)
+    for b in range(B):
+        p = int(pos[b])
+        if p < 0:
+            continue
         n_valid = min(p + 1, C)
         vals = state.values(b)
         for j in range(cfg.n_q_heads):

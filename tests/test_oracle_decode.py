@@ -144,3 +144,32 @@ def test_position_mismatch_sets_error_and_applies_step_at_pos():
     _, err = decode_step(state, rng.standard_normal((1, 4, 16)), rng.standard_normal((1, 2, 16)),
                          rng.standard_normal((1, 2, 16)), np.array([3]))
     assert err and state.n_tokens[0] == 4 and (state.slot_pos[0, :, 3] == 3).all()
+
+
+def test_decode_write_updates_only_the_ring_slot():
+    # the write half of a step: the rotated key rounded to bf16 in slot
+    # ring_slot(pos), the value copied, slot_pos and n_tokens advanced; an
+    # inactive row and every other slot untouched; a stale pos is flagged
+    from oracle import decode_write, ring_slot, rope_rotate, round_to_bf16
+    cfg = Config(n_q_heads=2, n_kv_heads=1, d_qk=4, d_v=4, L_sink=1, K=2, L_recent=3, W=1,
+                 pool=1, rope_theta=1e4, rope_begin=0, rope_end=4, dtype="bf16")
+    st = CacheState(cfg, 2)
+    rng = np.random.default_rng(3)
+    st.k[:] = round_to_bf16(rng.standard_normal(st.k.shape))
+    st.v[:] = round_to_bf16(rng.standard_normal(st.v.shape))
+    st.n_tokens[:] = [9, 4]
+    before_k, before_v = st.k.copy(), st.v.copy()
+    kn = round_to_bf16(rng.standard_normal((2, 1, 4)))
+    vn = round_to_bf16(rng.standard_normal((2, 1, 4)))
+    err = decode_write(st, kn, vn, np.array([9, -1]))
+    assert not err
+    slot = 1 + 2 + (9 - 3) % 3
+    assert slot == ring_slot(9, 1, 2, 3) == 3
+    np.testing.assert_array_equal(st.k[0, 0, slot], round_to_bf16(rope_rotate(kn[0], 9, 1e4, 0, 4))[0])
+    np.testing.assert_array_equal(st.v[0, 0, slot], vn[0, 0])
+    others = [s for s in range(cfg.C) if s != slot]
+    np.testing.assert_array_equal(st.k[0, :, others], before_k[0, :, others])
+    np.testing.assert_array_equal(st.k[1], before_k[1])
+    np.testing.assert_array_equal(st.v[1], before_v[1])
+    assert list(st.n_tokens) == [10, 4] and st.slot_pos[0, 0, slot] == 9
+    assert decode_write(st, kn, vn, np.array([12, -1]))   # n_tokens is 10: stale

@@ -127,3 +127,28 @@ def test_tiny_workload_regression_fixture():
     np.testing.assert_array_equal(res.sel, gold["sel"])
     np.testing.assert_array_equal(res.slot_pos, gold["slot_pos"])
     np.testing.assert_allclose(res.raw.sum(axis=1), gold["raw_sum"], rtol=1e-12)
+
+
+def test_layout_from_a_given_selection_hand_computed():
+    # L = 20, S = 2, K = 3, R = 5 (C = 10); kept middle indices 0, 4, 7 are
+    # tokens 2, 6, 9; the recent tokens 15..19 go to 5 + ((t - 5) mod 5),
+    # i.e. slots 5..9 in order.  Written out by hand, not from ring_slot.
+    from oracle import fixed_cache_layout
+    cfg = Config(n_q_heads=2, n_kv_heads=2, d_qk=3, d_v=2, L_sink=2, K=3, L_recent=5, W=1,
+                 pool=1)
+    rng = np.random.default_rng(0)
+    k = rng.standard_normal((2, 20, 3))
+    v = rng.standard_normal((2, 20, 2))
+    sel = np.array([[0, 4, 7], [1, 2, 12]])
+    kc, vc, sp = fixed_cache_layout(cfg, k, v, sel)
+    expect = [[0, 1, 2, 6, 9, 15, 16, 17, 18, 19], [0, 1, 3, 4, 14, 15, 16, 17, 18, 19]]
+    np.testing.assert_array_equal(sp, np.array(expect))
+    for h in range(2):
+        np.testing.assert_array_equal(kc[h], k[h, expect[h]])
+        np.testing.assert_array_equal(vc[h], v[h, expect[h]])
+    # and the oracle's own prefill lays out its own selection the same way
+    q = rng.standard_normal((2, 1, 3))
+    res = prefill_compress_one(cfg, q, k, v)
+    kc2, vc2, sp2 = fixed_cache_layout(cfg, k, v, res.sel)
+    np.testing.assert_array_equal(sp2, res.slot_pos)
+    np.testing.assert_array_equal(kc2, res.k_cache)
