@@ -26,3 +26,32 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # the tie-band counts of the selection comparisons (GPU parity tests):
+    # per test, the groups compared, |A| in total and at most, and the in-band
+    # swaps (out-of-band differences fail the test itself)
+    try:
+        import parity
+    except Exception:  # pragma: no cover
+        return
+    if not parity.TIE_LOG:
+        return
+    import json
+    agg = {}
+    for r in parity.TIE_LOG:
+        a = agg.setdefault(r["test"], {"groups": 0, "band_total": 0, "band_max": 0,
+                                        "swaps_total": 0, "swaps_max": 0, "m": r["m"], "K": r["K"]})
+        a["groups"] += 1
+        a["band_total"] += r["band"]
+        a["band_max"] = max(a["band_max"], r["band"])
+        a["swaps_total"] += r["swaps"]
+        a["swaps_max"] = max(a["swaps_max"], r["swaps"])
+    out = os.path.join(ROOT, "gpurun_out")
+    try:
+        os.makedirs(out, exist_ok=True)
+        with open(os.path.join(out, "tie_band.json"), "w") as f:
+            json.dump(agg, f, indent=1)
+    except OSError:  # pragma: no cover
+        pass

@@ -13,6 +13,7 @@ Comparison rules:
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import torch
@@ -23,6 +24,11 @@ import oracle
 
 TIE_BAND = 1e-6
 OUT_TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+# one record per compared (request, kv-head) selection: the test, |A| (keys
+# within the band of the K-th pooled score) and the in-band swaps; written to
+# gpurun_out/tie_band.json at the end of the session (tests/conftest.py)
+TIE_LOG = []
 
 
 def oracle_config(w: dict) -> oracle.Config:
@@ -55,6 +61,9 @@ def compare_selection(gpu_sel, pooled, oracle_sel, K):
     assert in_a[0].sum() == in_a[1].sum()
     assert np.all(np.diff(gpu_sel) > 0), "selection must be ascending and unique"
     swaps = len(set(gpu_sel.tolist()) ^ set(oracle_sel.tolist())) // 2
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    TIE_LOG.append({"test": test, "m": int(len(pooled)), "K": int(K), "band": int(band.sum()),
+                    "swaps": int(swaps)})
     return int(band.sum()), swaps
 
 

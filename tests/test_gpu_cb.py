@@ -1,13 +1,18 @@
 """GPU parity of continuous batching against the fp64 oracle: a static batch of
 cache rows whose requests have different prompt lengths (log-uniform), some
 stored uncompressed and some compressed, decoding together; at set steps a
-row's request is replaced by a newly admitted prompt, compressed into that
-row by a single-row prefill call while the other rows keep decoding.
+row's request finishes and a new prompt is compressed into that row by a
+single-row prefill call while the other rows keep decoding.
 
-Per followed row: the library's prefill (selection under the tie-band rule,
-slot map) is checked against the oracle's; the decode comparison then starts
-both sides from the oracle's cache row (uploaded bit-exactly), and every step
-checks the output (max-abs <= 2e-2, bf16), the written slot and n_tokens."""
+The library decodes from its own caches: nothing is uploaded from the oracle.
+For every followed row, each admission is checked against the oracle's
+prefill (selection under the tie-band rule); the oracle's row is then the
+fixed layout of the library's validated selection (it differs from the
+oracle's own only inside the band), and the library's cache row must be a
+bit-exact copy of it.  On the checked steps the oracle runs the full decode
+step of the followed rows (outputs within max-abs 2e-2, bf16, and the written
+slot bit-exact); on the other steps it applies only the cache write, so both
+caches stay in step."""
 import numpy as np
 import pytest
 import torch
@@ -15,116 +20,145 @@ import torch
 import oracle
 from kv_cache_compression_obs_amd import snapstream as ss
 from kv_cache_compression_obs_amd import synth
-from parity import (OUT_TOL, compare_selection, lib_config, oracle_config, oracle_prefill_request,
-                    say)
+from parity import OUT_TOL, compare_selection, lib_config, oracle_config, oracle_prefill_request, say
 
 pytestmark = pytest.mark.gpu
 
 
-def _lib_admit(cfg, w, cache, row, inp):
+def _admit(w, cfg, cache, row, inp, state=None, i=None):
+    """One request into cache row `row` through the library; when `state` is
+    given (a followed row), check it against the oracle and make oracle row i
+    the layout of the validated selection."""
     L = inp["k"].shape[2]
-    m = L - w["L_sink"] - w["L_recent"]
     sel = None
     if L > w["C"]:
         sel = torch.full((1, w["n_kv_heads"], w["K"]), -1, dtype=torch.int32, device="cuda")
-        pooled = torch.empty(1, w["n_kv_heads"], m, device="cuda")
     rows = torch.tensor([row], dtype=torch.int32, device="cuda")
-    ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], cache, rows=rows,
-                           pooled_out=pooled if sel is not None else None, sel_out=sel)
-    return sel
-
-
-def _follow(w, cache, state, i, row, inp, sel):
-    """Check the library's admission of one followed row against the oracle,
-    then give both sides the oracle's row."""
+    ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], cache, rows=rows, sel_out=sel)
+    if state is None:
+        return
     res = oracle_prefill_request(w, inp, 0)
     torch.cuda.synchronize()
     if sel is not None:
+        sel_lib = sel[0].cpu().numpy().astype(np.int64)
         for h in range(w["n_kv_heads"]):
-            compare_selection(sel[0, h].cpu().numpy(), res.pooled[h], res.sel[h], w["K"])
+            compare_selection(sel_lib[h], res.pooled[h], res.sel[h], w["K"])
+        k = synth.to_f64(inp["k"][0])
+        v = synth.to_f64(inp["v"][0])
+        k_c, v_c, sp = oracle.fixed_cache_layout(oracle_config(w), k, v, sel_lib)
+        del k, v
     else:
-        np.testing.assert_array_equal(cache.slot_pos[row].cpu().numpy(), res.slot_pos)
-    assert int(cache.n_tokens[row].item()) == res.n_tokens
-    state.admit(i, res)
-    dt = cache.k.dtype
-    cache.k[row].copy_(torch.from_numpy(res.k_cache).to(dt))
-    cache.v[row].copy_(torch.from_numpy(res.v_cache).to(dt))
-    cache.slot_pos[row].copy_(torch.from_numpy(res.slot_pos).to(torch.int32))
+        k_c, v_c, sp = res.k_cache, res.v_cache, res.slot_pos
+    np.testing.assert_array_equal(cache.slot_pos[row].cpu().numpy(), sp)
+    assert int(cache.n_tokens[row].item()) == L
+    n = min(L, w["C"])
+    assert np.array_equal(cache.k[row, :, :n].double().cpu().numpy(), k_c[:, :n])
+    assert np.array_equal(cache.v[row, :, :n].double().cpu().numpy(), v_c[:, :n])
+    state.k[i], state.v[i], state.slot_pos[i], state.n_tokens[i] = k_c, v_c, sp, L
 
 
-def _cb_case(w, seed, steps, admissions, adm_len, follow):
-    """admissions: {step: row}; follow: rows the oracle tracks."""
+def _cb_case(w, seed, admissions, follow, check, steps=None):
+    """admissions: {step: row}; follow: rows the oracle tracks; check(t):
+    whether step t compares outputs (other steps apply the oracle's write)."""
     B, C = w["B"], w["C"]
+    steps = steps or w["steps"]
     cfg = lib_config(w)
     lens = synth.request_lengths(w, seed, B)
     say(f"cb {w['name']} B={B} C={C} lengths {min(lens)}..{max(lens)} "
-        f"({sum(n > C for n in lens)} compressed), follow {follow}")
+        f"({sum(n > C for n in lens)} compressed), {steps} steps, admissions {admissions}, "
+        f"follow {follow}")
     cache = ss.Cache(cfg, B)
     state = oracle.CacheState(oracle_config(w), len(follow))
-    n_tok = np.zeros(B, dtype=np.int64)
     for r in range(B):
         inp = synth.prefill_inputs(w, seed * 1000 + r, device="cuda", B=1, L=lens[r])
-        sel = _lib_admit(cfg, w, cache, r, inp)
         if r in follow:
-            _follow(w, cache, state, follow.index(r), r, inp, sel)
-        n_tok[r] = lens[r]
+            _admit(w, cfg, cache, r, inp, state, follow.index(r))
+        else:
+            _admit(w, cfg, cache, r, inp)
         del inp
+    n_tok = np.array(lens, dtype=np.int64)
     dec = synth.decode_inputs(w, seed, steps, device="cuda", B=B)
     out = torch.empty(B, w["n_q_heads"], w["d_v"], dtype=torch.bfloat16, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = ss.decode_workspace(cfg, B)
     fidx = torch.tensor(follow, device="cuda")
-    worst = 0.0
+    worst, n_checked = 0.0, 0
     for t in range(steps):
         if t in admissions:
             row = admissions[t]
-            inp = synth.prefill_inputs(w, seed * 1000 + 500 + t, device="cuda", B=1, L=adm_len)
-            sel = _lib_admit(cfg, w, cache, row, inp)
+            inp = synth.prefill_inputs(w, seed * 1000 + 500 + t, device="cuda", B=1, L=w["L"])
             if row in follow:
-                _follow(w, cache, state, follow.index(row), row, inp, sel)
-            n_tok[row] = adm_len
+                _admit(w, cfg, cache, row, inp, state, follow.index(row))
+            else:
+                _admit(w, cfg, cache, row, inp)
+            n_tok[row] = w["L"]
             del inp
         pos = torch.from_numpy(n_tok.astype(np.int32)).cuda()
         ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], dec["v_new"][t], pos, cache, out,
                           err, ws)
-        ref, ref_err = oracle.decode_step(state, synth.to_f64(dec["q"][t][fidx]),
-                                          synth.to_f64(dec["k_new"][t][fidx]),
-                                          synth.to_f64(dec["v_new"][t][fidx]), n_tok[follow])
-        torch.cuda.synchronize()
-        got = out[fidx].double().cpu().numpy()
-        diff = np.abs(got - ref).max()
-        worst = max(worst, diff)
-        assert diff <= OUT_TOL["bf16"], f"step {t}: max-abs {diff:.3g}"
+        kn = synth.to_f64(dec["k_new"][t][fidx])
+        vn = synth.to_f64(dec["v_new"][t][fidx])
+        if check(t):
+            ref, ref_err = oracle.decode_step(state, synth.to_f64(dec["q"][t][fidx]), kn, vn,
+                                              n_tok[follow])
+            torch.cuda.synchronize()
+            diff = np.abs(out[fidx].double().cpu().numpy() - ref).max()
+            worst = max(worst, diff)
+            n_checked += 1
+            assert diff <= OUT_TOL["bf16"], f"step {t}: max-abs {diff:.3g}"
+            for i, r in enumerate(follow):
+                slot = oracle.ring_slot(int(n_tok[r]), w["L_sink"], w["K"], w["L_recent"])
+                np.testing.assert_array_equal(cache.k[r, :, slot].double().cpu().numpy(),
+                                              state.k[i, :, slot])
+                np.testing.assert_array_equal(cache.v[r, :, slot].double().cpu().numpy(),
+                                              state.v[i, :, slot])
+        else:
+            ref_err = oracle.decode_write(state, kn, vn, n_tok[follow])
         assert not ref_err
-        for i, r in enumerate(follow):
-            slot = oracle.ring_slot(int(n_tok[r]), w["L_sink"], w["K"], w["L_recent"])
-            np.testing.assert_array_equal(cache.k[r, :, slot].double().cpu().numpy(),
-                                          state.k[i, :, slot])
-            np.testing.assert_array_equal(cache.slot_pos[r].cpu().numpy(), state.slot_pos[i])
         n_tok += 1
+    torch.cuda.synchronize()
     assert int(err.item()) == 0
     np.testing.assert_array_equal(cache.n_tokens.cpu().numpy(), n_tok)
-    say(f"  worst max-abs {worst:.3g}")
+    for i, r in enumerate(follow):  # whole followed rows, after every write
+        np.testing.assert_array_equal(cache.slot_pos[r].cpu().numpy(), state.slot_pos[i])
+        assert np.array_equal(cache.k[r].double().cpu().numpy(), state.k[i])
+        assert np.array_equal(cache.v[r].double().cpu().numpy(), state.v[i])
+    say(f"  {n_checked} steps checked, worst max-abs {worst:.3g}")
 
 
 def test_continuous_batching_small():
     # 6 rows, C = 1024, prompts log-uniform in [64, 4096] (some compressed,
     # some stored as they are), two admissions of 2048-token prompts; the
-    # oracle follows every row at every step
+    # oracle follows every row and checks every step
     w = synth.workload("llama8b_cb64", B=6, L_sink=16, K=240, L_recent=768, len_min=64,
-                       len_max=4096)
-    _cb_case(w, seed=31, steps=60, admissions={20: 1, 40: 4}, adm_len=2048,
-             follow=list(range(6)))
+                       len_max=4096, L=2048)
+    _cb_case(w, seed=31, admissions={20: 1, 40: 4}, follow=list(range(6)), check=lambda t: True,
+             steps=60)
 
 
-def test_continuous_batching_full_shape_sampled_rows():
-    # 64 rows x C = 32768, prompts log-uniform in [1k, 128k], a 65536-token
-    # admission mid-run; the oracle follows a compressed row, an uncompressed
-    # row and the admitted row
+def test_continuous_batching_as_specified():
+    # the full workload: 64 rows x C = 32768, prompts log-uniform in
+    # [1k, 128k] set up through ss_prefill_compress, 1000 decode steps, and
+    # before steps 200/400/600/800 a seeded row's request is replaced by a new
+    # 65536-token prompt.  Followed: a compressed row (mid-eviction), a row
+    # below capacity (masked slots), the first admitted row (before and after
+    # its admission) and, if one exists, a row that crosses capacity during
+    # the run.  Checked: the first 8 steps, the 3 steps from each admission
+    # (and the one before it), the last 8.
     w = synth.workload("llama8b_cb64")
-    lens = synth.request_lengths(w, 32, w["B"])
-    long_row = next(r for r, n in enumerate(lens) if n > w["C"])
-    short_row = next(r for r, n in enumerate(lens) if n < w["C"])
-    adm_row = next(r for r in range(w["B"]) if r not in (long_row, short_row))
-    _cb_case(w, seed=32, steps=8, admissions={4: adm_row}, adm_len=65536,
-             follow=[long_row, short_row, adm_row])
+    seed = 41
+    C, steps = w["C"], w["steps"]
+    lens = synth.request_lengths(w, seed, w["B"])
+    adm_rows = synth.admission_rows(w, seed)
+    admissions = dict(zip(w["admissions"], adm_rows))
+    free = [r for r in range(w["B"]) if r not in adm_rows]
+    follow = [next(r for r in free if lens[r] > C),
+              next(r for r in free if lens[r] < C - steps),
+              adm_rows[0]]
+    cross = [r for r in free if C - steps < lens[r] < C]
+    if cross:
+        follow.append(cross[0])
+    checked = set(range(8)) | set(range(steps - 8, steps))
+    for a in admissions:
+        checked |= set(range(a - 1, a + 3))
+    _cb_case(w, seed, admissions, follow, check=lambda t: t in checked)

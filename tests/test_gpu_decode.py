@@ -1,7 +1,8 @@
 """GPU parity of ss_decode_step against the fp64 oracle.
 
 Both sides start from the oracle's prefill state (uploaded bit-exactly), then
-take the same seeded decode inputs step by step.  Checked every step: the
+take the same seeded decode inputs step by step; one full-shape test instead
+decodes from the library's own prefill (see there).  Checked every step: the
 attention output (max-abs <= 1e-4 fp32, <= 2e-2 bf16), the written slot of
 every row (slot_pos exact, rotated key and value bit-exact), n_tokens."""
 import numpy as np
@@ -10,7 +11,7 @@ import torch
 
 from kv_cache_compression_obs_amd import snapstream as ss
 from kv_cache_compression_obs_amd import synth
-from parity import decode_case, lib_config, say
+from parity import OUT_TOL, decode_case, lib_config, say
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +124,61 @@ def test_decode_is_deterministic_and_workspace_reusable():
     assert torch.equal(cache.slot_pos, twin.slot_pos)
     counters = ws[:4 * 8 * 4].view(torch.int32)
     assert int(counters.abs().sum().item()) == 0
+
+
+def test_decode_from_library_prefill_llama8b_c4k():
+    # the library's own prefill-then-decode chain at full shape (16 x 8
+    # groups, 16384 -> 4096 slots): nothing is uploaded from the oracle.  Two
+    # requests are followed: their selections are checked against the oracle
+    # under the tie-band rule, their cache rows must be bit-exact copies of the
+    # layout of the validated selection, and every one of 24 decode steps is
+    # compared (outputs, written slot, token count)
+    import oracle
+    from parity import compare_selection, oracle_config, oracle_prefill_request
+    w = synth.workload("llama8b_c4k")
+    B, C, H = w["B"], w["C"], w["n_kv_heads"]
+    cfg = lib_config(w)
+    inp = synth.prefill_inputs(w, 81, device="cuda")
+    cache = ss.Cache(cfg, B)
+    sel = torch.full((B, H, w["K"]), -1, dtype=torch.int32, device="cuda")
+    ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], cache, sel_out=sel)
+    follow = [3, 12]
+    state = oracle.CacheState(oracle_config(w), len(follow))
+    for i, bi in enumerate(follow):
+        res = oracle_prefill_request(w, inp, bi)
+        sel_lib = sel[bi].cpu().numpy().astype(np.int64)
+        for h in range(H):
+            compare_selection(sel_lib[h], res.pooled[h], res.sel[h], w["K"])
+        k_c, v_c, sp = oracle.fixed_cache_layout(oracle_config(w), synth.to_f64(inp["k"][bi]),
+                                                 synth.to_f64(inp["v"][bi]), sel_lib)
+        np.testing.assert_array_equal(cache.slot_pos[bi].cpu().numpy(), sp)
+        assert np.array_equal(cache.k[bi].double().cpu().numpy(), k_c)
+        assert np.array_equal(cache.v[bi].double().cpu().numpy(), v_c)
+        state.k[i], state.v[i], state.slot_pos[i], state.n_tokens[i] = k_c, v_c, sp, w["L"]
+    steps = 24
+    dec = synth.decode_inputs(w, 81, steps, device="cuda")
+    out = torch.empty(B, w["n_q_heads"], w["d_v"], dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = ss.decode_workspace(cfg, B)
+    fidx = torch.tensor(follow, device="cuda")
+    worst = 0.0
+    for t in range(steps):
+        p = w["L"] + t
+        ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], dec["v_new"][t],
+                          torch.full((B,), p, dtype=torch.int32, device="cuda"), cache, out, err,
+                          ws)
+        ref, ref_err = oracle.decode_step(state, synth.to_f64(dec["q"][t][fidx]),
+                                          synth.to_f64(dec["k_new"][t][fidx]),
+                                          synth.to_f64(dec["v_new"][t][fidx]), np.full(2, p))
+        torch.cuda.synchronize()
+        diff = np.abs(out[fidx].double().cpu().numpy() - ref).max()
+        worst = max(worst, diff)
+        assert diff <= OUT_TOL["bf16"], f"step {t}: max-abs {diff:.3g}"
+        slot = oracle.ring_slot(p, w["L_sink"], w["K"], w["L_recent"])
+        for i, bi in enumerate(follow):
+            np.testing.assert_array_equal(cache.k[bi, :, slot].double().cpu().numpy(),
+                                          state.k[i, :, slot])
+        assert not ref_err
+    assert int(err.item()) == 0
+    assert np.all(cache.n_tokens.cpu().numpy() == w["L"] + steps)
+    say(f"  decode from the library's prefill: worst max-abs {worst:.3g}")
