@@ -117,9 +117,15 @@ __device__ __forceinline__ void wave_sync() {
 // Ordering: every writer waits for its partial stores to complete at the
 // device-coherent level before it takes its ticket; the merging workgroup
 // holds the last ticket, so all partials are there before it issues its
-// device-scope loads (ld_dev).  No acquire fence is needed: a fence would
+// device-scope loads (ld_dev).  No acquire fence is used: a fence would
 // invalidate this XCD's whole L2 and slow every workgroup still streaming on
-// it.  The merge computes
+// it.  This rests on the gfx942/gfx950 cache policy rather than on the HIP
+// memory model's release/acquire pair: sc1 stores (agent-scope atomic stores
+// and st_dev4) write through the XCD's L2, s_waitcnt vmcnt(0) returns once
+// they are acknowledged at the device-coherent level, and sc1 loads
+// (agent-scope atomic loads and ld_dev4) never hit a stale line of this XCD's
+// L2.  Checked with the ROCm 7.2 toolchain; the determinism, many-split and
+// graph-replay decode tests guard it.  The merge computes
 //   out[head, dv] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
 // in split order.
 template <typename T, int DV, int NI>
