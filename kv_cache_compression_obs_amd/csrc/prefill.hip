@@ -483,13 +483,20 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
 // Build the cache rows of one request: slots [0, S) <- tokens 0..S-1, slots
 // [S, S+K) <- the selected middle tokens (ascending), ring slots <- the last R
 // tokens at S+K + ((t-S-K) mod R).  Uncompressed prompts (L <= C) map token t
-// to slot t.  Grid (cdiv(C, 16), Hkv, b); copies are 16-byte coalesced.
-// A destination row outside [0, B_max) is skipped.
+// to slot t.  Grid (cdiv(C, GATHER_SLOTS), Hkv, b), 256 threads.  Each
+// thread issues all of its 16-byte loads (K, then V rows) before its first
+// store, so a workgroup has its whole 64-slot block in flight at once; the
+// prompt rows are read once, with the non-temporal hint.  A destination row
+// outside [0, B_max) is skipped.
+constexpr int GATHER_SLOTS = 64;
+
 template <typename T, int D, int DV, bool ALIAS>
 __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compressed) {
-  constexpr int SLOTS = 16;
+  constexpr int SLOTS = GATHER_SLOTS;
   constexpr int KCH = D * static_cast<int>(sizeof(T)) / 16;
-  constexpr int VCH = DV * static_cast<int>(sizeof(T)) / 16;
+  constexpr int VCH = ALIAS ? 0 : DV * static_cast<int>(sizeof(T)) / 16;
+  constexpr int NK = SLOTS * KCH / 256, NV = SLOTS * VCH / 256;  // units per thread
+  static_assert(SLOTS * KCH % 256 == 0 && SLOTS * VCH % 256 == 0, "whole units per thread");
   __shared__ int tok[SLOTS];
   const int tid = threadIdx.x;
   const int sb = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
@@ -524,24 +531,38 @@ __global__ __launch_bounds__(256) void gather_kernel(PrefillArgs a, int compress
   __syncthreads();
   const char* ksrc = reinterpret_cast<const char*>(static_cast<const T*>(a.k) + pr.row0 * D);
   char* kdst = reinterpret_cast<char*>(static_cast<T*>(a.kc) + gdst * a.C * D);
-  for (int id = tid; id < SLOTS * KCH; id += blockDim.x) {
-    const int j = id / KCH, ch = id % KCH;
-    const int t = tok[j];
-    if (t < 0) continue;
-    const size_t s = static_cast<size_t>(sb) * SLOTS + j;
-    *reinterpret_cast<u32x4_t*>(kdst + s * KCH * 16 + ch * 16) =
-        *reinterpret_cast<const u32x4_t*>(ksrc + static_cast<size_t>(t) * KCH * 16 + ch * 16);
+  const char* vsrc = ALIAS ? nullptr
+                           : reinterpret_cast<const char*>(static_cast<const T*>(a.v) + pr.row0 * DV);
+  char* vdst = ALIAS ? nullptr : reinterpret_cast<char*>(static_cast<T*>(a.vc) + gdst * a.C * DV);
+  // unit id = i * 256 + tid: slot id / KCH of the block, chunk id % KCH
+  u32x4_t kv[NK], vv[NV > 0 ? NV : 1];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int id = i * 256 + tid, t = tok[id / KCH];
+    if (t >= 0)
+      kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+          ksrc + static_cast<size_t>(t) * KCH * 16 + (id % KCH) * 16));
   }
-  if (ALIAS) return;
-  const char* vsrc = reinterpret_cast<const char*>(static_cast<const T*>(a.v) + pr.row0 * DV);
-  char* vdst = reinterpret_cast<char*>(static_cast<T*>(a.vc) + gdst * a.C * DV);
-  for (int id = tid; id < SLOTS * VCH; id += blockDim.x) {
-    const int j = id / VCH, ch = id % VCH;
-    const int t = tok[j];
-    if (t < 0) continue;
-    const size_t s = static_cast<size_t>(sb) * SLOTS + j;
-    *reinterpret_cast<u32x4_t*>(vdst + s * VCH * 16 + ch * 16) =
-        *reinterpret_cast<const u32x4_t*>(vsrc + static_cast<size_t>(t) * VCH * 16 + ch * 16);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int id = i * 256 + tid, t = tok[id / VCH];
+    if (t >= 0)
+      vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+          vsrc + static_cast<size_t>(t) * VCH * 16 + (id % VCH) * 16));
+  }
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int id = i * 256 + tid;
+    if (tok[id / KCH] >= 0)
+      *reinterpret_cast<u32x4_t*>(kdst + (static_cast<size_t>(sb) * SLOTS + id / KCH) * KCH * 16 +
+                                  (id % KCH) * 16) = kv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int id = i * 256 + tid;
+    if (tok[id / VCH] >= 0)
+      *reinterpret_cast<u32x4_t*>(vdst + (static_cast<size_t>(sb) * SLOTS + id / VCH) * VCH * 16 +
+                                  (id % VCH) * 16) = vv[i];
   }
 }
 
@@ -584,7 +605,8 @@ hipError_t run_scores(const PrefillArgs& a, hipStream_t st, hipEvent_t ev0, hipE
 
 template <typename T, int D, int DV, bool ALIAS>
 hipError_t run_gather(bool compressed, const PrefillArgs& a, hipStream_t st) {
-  gather_kernel<T, D, DV, ALIAS><<<dim3(cdiv(a.C, 16), a.Hkv, a.b), 256, 0, st>>>(a, compressed);
+  gather_kernel<T, D, DV, ALIAS>
+      <<<dim3(cdiv(a.C, GATHER_SLOTS), a.Hkv, a.b), 256, 0, st>>>(a, compressed);
   return hipGetLastError();
 }
 
