@@ -155,6 +155,63 @@ struct KeyRing {
   }
 };
 
+// One tile's contraction as NS steps (step s: key block s / NC, k-chunk
+// s % NC; one fragment read from LDS and NMF MFMAs that use it).  With
+// GS > 0 the fragments are double-buffered in groups of GS steps: the reads
+// of group g + 1 are issued right after the MFMAs of the first step of group
+// g, an order pinned with sched_group_barrier.  The pinning matters because
+// the compiler drains every outstanding LDS read (lgkmcnt(0)) before the
+// first use of any fragment while direct global->LDS loads are in flight (it
+// cannot tell their LDS writes from the reads); placed this way, that drain
+// finds reads issued a group earlier.  GS = 0: each fragment is read where
+// it is used.
+#ifndef SS_SCORE_GS
+#define SS_SCORE_GS 3
+#endif
+// steps per fragment group for the two-block (latent) shape; 0 elsewhere
+template <int RB>
+constexpr int contract_group() { return RB == 2 ? SS_SCORE_GS : 0; }
+
+template <int NS, int GS, typename Frag, typename Read, typename Step>
+__device__ __forceinline__ void contract_steps(Read&& read, Step&& step) {
+  if constexpr (GS == 0) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) step(read(st), st);
+  } else {
+    static_assert(NS % GS == 0, "steps per group");
+    constexpr int NG = NS / GS;
+    Frag kb[2][GS];
+#pragma unroll
+    for (int c = 0; c < GS; ++c) kb[0][c] = read(c);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int c = 0; c < GS; ++c) {
+        step(kb[g & 1][c], g * GS + c);
+        if (c == 0 && g + 1 < NG) {
+#pragma unroll
+          for (int c2 = 0; c2 < GS; ++c2) kb[(g + 1) & 1][c2] = read((g + 1) * GS + c2);
+        }
+      }
+    }
+  }
+}
+
+template <int NS, int GS, int NMF>
+__device__ __forceinline__ void pin_contract_order() {
+  if constexpr (GS > 0) {
+    constexpr int NG = NS / GS;
+#pragma unroll
+    for (int c = 0; c < GS; ++c) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);                     // MFMA
+      if (g + 1 < NG) __builtin_amdgcn_sched_group_barrier(0x100, GS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF * (GS - 1), 0);
+    }
+  }
+}
+
 // Q_obs rows of the group (G heads x W rows, contiguous) as A fragments.
 template <typename T, int D>
 __device__ __forceinline__ void load_q(typename Mma<T>::frag (&qf)[D / Mma<T>::KSTEP],
@@ -190,6 +247,7 @@ void score_rowstat_kernel(PrefillArgs a) {
   using Ring = KeyRing<T, D, KT, NWV, NBUF>;
   constexpr int NC = D / MM::KSTEP;
   constexpr int NKB = KT / 16;
+  constexpr int GS = contract_group<RB>();
   constexpr float LAZY = 8.f;
   constexpr float EMPTY = -0x1p126f;  // m of a row that has seen no key yet (finite: no inf - inf)
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * Ring::BYTES];
@@ -245,16 +303,17 @@ void score_rowstat_kernel(PrefillArgs a) {
       const char* cur = lds + sl * Ring::BYTES;
       f32x4_t acc[RB][NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) acc[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      contract_steps<NKB * NC, GS, typename MM::frag>(
+          [&](int st) __attribute__((always_inline)) { return Ring::bfrag(cur, lt, st / NC, st % NC); },
+          [&](typename MM::frag kf, int st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const typename MM::frag kf = Ring::bfrag(cur, lt, kb, c);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[rb][kb] = MM::mma(qf[rb][c], kf, acc[rb][kb]);
-        }
-      }
+            for (int rb = 0; rb < RB; ++rb)
+              acc[rb][st / NC] = MM::mma(qf[rb][st % NC], kf, acc[rb][st / NC]);
+          });
+      pin_contract_order<NKB * NC, GS, RB>();
       if (t0 + KT > open_end) {  // (uniform) the ragged end or the causal window
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -390,6 +449,7 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
   using Ring = KeyRing<T, D, KT, NWV, NBUF>;
   constexpr int NC = D / MM::KSTEP;
   constexpr int NKB = KT / 16;
+  constexpr int GS = contract_group<RB>();
   // one LDS object: the ring, then the column partials red[NBUF][NWV][KT]
   // (with a second object the compiler adds a full vmcnt wait before every
   // read of the ring)
@@ -450,23 +510,27 @@ __global__ __launch_bounds__(64 * NWV) void score_columns_kernel(PrefillArgs a) 
       if (t0 > k0) columns_out(t0 - KT, (sl + NBUF - 1) % NBUF);
       if (!active) continue;
       const char* cur = lds + sl * Ring::BYTES;
+      f32x4_t acc[RB][NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      contract_steps<NKB * NC, GS, typename MM::frag>(
+          [&](int st) __attribute__((always_inline)) { return Ring::bfrag(cur, lt, st / NC, st % NC); },
+          [&](typename MM::frag kf, int st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              acc[rb][st / NC] = MM::mma(qf[rb][st % NC], kf, acc[rb][st / NC]);
+          });
+      pin_contract_order<NKB * NC, GS, RB>();
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        f32x4_t acc[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const typename MM::frag kf = Ring::bfrag(cur, lt, kb, c);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[rb] = MM::mma(qf[rb][c], kf, acc[rb]);
-        }
         float cs = 0.f;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            cs = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[rb][r], sc, nM[rb][r])), w[rb][r],
+            cs = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[rb][kb][r], sc, nM[rb][r])), w[rb][r],
                                 cs);
         cs = sum_across_16(cs);
         cs = sum_across_32(cs);

@@ -29,6 +29,13 @@ def test_mla_prefill_small_ragged():
     prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512), 21, L=4999)
 
 
+@pytest.mark.parametrize("W", [8, 20])
+def test_mla_prefill_fewer_score_rows(W):
+    # G*W = 64 or 160 score rows: the 64-row waves of the latent passes are
+    # partly padding or idle; L = 3001 gives a ragged last tile in both passes
+    prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512, W=W), 35 + W, L=3001)
+
+
 def test_mla_prefill_given_lse_one_pass():
     prefill_case(_mla(B=2, L_sink=16, K=200, L_recent=512), 29, L=4999, given_lse=True)
 
