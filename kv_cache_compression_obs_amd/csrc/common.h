@@ -124,6 +124,19 @@ __device__ __forceinline__ float sum_across_32(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// the maximum of v and the value of lane l ^ 16 (resp. l ^ 32), through the
+// same row swaps
+__device__ __forceinline__ float max_across_16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_across_32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace ss

@@ -9,7 +9,9 @@
 // rank's share: G heads against the rank's whole latent cache).
 //
 // One workgroup of 4 waves per (split of the slots, row).  Per 32-slot tile
-// the latent rows are staged once in LDS and used twice:
+// the latent rows are brought into LDS by direct global->LDS loads (no
+// registers: the next tile streams into the other half of a two-tile ring
+// while this one is used) and used twice:
 //   S^T[slot, head] = Lat[slot, 0:576] . Q[head, :]^T   - the 18 d-chunks of
 //       32 are spread over the 4 waves and the partial sums added through LDS
 //       (every wave adds them in the same order, so all hold the same S);
@@ -17,7 +19,15 @@
 //       value dims [128w, 128w + 128).
 // Rotary embedding at pos covers dims 512..575 (the rope range of the config);
 // the rotated latent row is written into the ring slot and patched into the
-// tile from LDS.  Partials, ticket and merge as in decode.hip.
+// tile from registers.  Partials, ticket and merge as in decode.hip.
+//
+// LDS round trips set the pace of a tile, so the fragment reads go out in
+// batches: all K fragments of a wave at once, the V fragments four at a time
+// with the gfx950 transposing reads (two per fragment instead of eight 2-byte
+// reads).  With direct loads in flight the compiler drains every vector-memory
+// load before an LDS read it cannot tell apart from them, so these batches
+// are asm blocks that also wait for their own reads, and the workgroup
+// barriers inside a tile wait for LDS accesses only.
 #include "decode_common.h"
 
 namespace ss {
@@ -31,13 +41,121 @@ constexpr int MNT = 64 * MW;            // threads per workgroup
 constexpr int MD = 576, MDV = 512;      // latent dims, value dims
 constexpr int MTS = DECODE_TILE;        // slots per tile
 constexpr int MROW = MD * 2;            // bytes of one latent row (bf16)
-constexpr int MLROW = MROW + 16;        // LDS row stride
-constexpr int MCH = MROW / 16;          // 16-byte chunks per row
-constexpr int MLD = MTS * MCH / MNT;    // chunks per thread per tile
+constexpr int MCH = MROW / 16;          // 16-byte units per row
+constexpr int MTB = MTS * MROW;         // bytes of one tile in LDS (rows not padded)
+constexpr int MNL = MTB / 1024;         // 1 KB direct loads per tile
+constexpr int MLW = MNL / MW;           // ... per wave
+static_assert(MTB % 1024 == 0 && MNL % MW == 0, "whole direct loads per wave");
+static_assert(MCH % 8 == 0, "the unit swizzle stays inside a row");
 constexpr int MNC = MD / 32;            // d-chunks of the Q.K^T contraction
 constexpr int MCW = cdiv(MNC, MW);      // at most this many chunks per wave
 constexpr int MNDB = MDV / 16 / MW;     // 16-wide value blocks per wave
-static_assert(MTS * MCH % MNT == 0, "tile split");
+constexpr int CPOL_NT = 2;              // cache policy nt: non-temporal (each row is read once)
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Tile layout in LDS: unit u (16 bytes) of tile row r sits at unit
+// r * MCH + (u ^ (r & 7)).  The rows are not padded (two tiles and the score
+// exchange fill exactly half of a CU's LDS, so two workgroups share a CU);
+// the XOR spreads the 16 rows that one fragment read touches over more
+// banks than the plain layout does.
+__device__ __forceinline__ int lat_byte(int r, int u) { return (r * MCH + (u ^ (r & 7))) * 16; }
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// V^T operands of the P.V contraction from the swizzled tile: lane
+// (col, qg) of fragment db takes value dim 16 db + col of tile rows 4 i + qg,
+// i < 8 (the slots the Q.K^T accumulator left in its P^T layout).  Two
+// transposing LDS reads (ds_read_b64_tr_b16) build one: within each group of
+// 16 lanes, lane 4a + b receives element b of the 8-byte chunks that lanes
+// a + 4k (k < 4) address.  So lane (qg, a = lane % 4, k = lane / 4 % 4)
+// addresses dims 16 db + 4a .. + 3 of row 4k + qg (elements i = k) and of row
+// 16 + 4k + qg (i = 4 + k).  The NV fragments' reads go out in one asm
+// block that ends by waiting for them: the compiler, which cannot tell these
+// reads from the direct loads still writing the other half of the ring,
+// would otherwise wait for every outstanding vector-memory load first.
+template <int NV>
+__device__ __forceinline__ void vfrags(const char* t, int db0, int lane, bf16x8_t (&out)[NV]) {
+  static_assert(NV == 4, "one asm block of 8 reads");
+  const int qg = lane >> 4, a = lane & 3, k = (lane >> 2) & 3;
+  int ad[2 * NV];
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int u = 2 * (db0 + q) + (a >> 1), byte = (a & 1) * 8;
+    const char* p0 = t + lat_byte(4 * k + qg, u) + byte;
+    const char* p1 = t + lat_byte(16 + 4 * k + qg, u) + byte;
+    ad[2 * q] = static_cast<int>((uintptr_t)((const __attribute__((address_space(3))) char*)p0));
+    ad[2 * q + 1] = static_cast<int>((uintptr_t)((const __attribute__((address_space(3))) char*)p1));
+  }
+  u32x2_t r[2 * NV];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7])
+      : "memory");
+#pragma unroll
+  for (int q = 0; q < NV; ++q)
+    out[q] = __builtin_bit_cast(bf16x8_t, u32x4_t{r[2 * q].x, r[2 * q].y, r[2 * q + 1].x,
+                                                  r[2 * q + 1].y});
+}
+
+// The 2 x MCW K fragments (A operands of S^T = K . Q^T) of a wave: tile
+// rows 16 h2 + koff, 16-byte unit 4 c + qg of d-chunk c = clo + j (clamped
+// to the last chunk).  One asm block issues the reads and waits for them,
+// for the reason given above.
+__device__ __forceinline__ void kfrags(const char* t, int koff, int clo, int qg,
+                                       bf16x8_t (&out)[2][MCW]) {
+  static_assert(MCW == 5, "one asm block of 10 reads");
+  int ad[2 * MCW];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int j = 0; j < MCW; ++j)
+      ad[h2 * MCW + j] = static_cast<int>((uintptr_t)((const __attribute__((address_space(3))) char*)(
+          t + lat_byte(16 * h2 + koff, 4 * min(clo + j, MNC - 1) + qg))));
+  u32x4_t r[2 * MCW];
+  asm volatile(
+      "ds_read_b128 %0, %10\n\t"
+      "ds_read_b128 %1, %11\n\t"
+      "ds_read_b128 %2, %12\n\t"
+      "ds_read_b128 %3, %13\n\t"
+      "ds_read_b128 %4, %14\n\t"
+      "ds_read_b128 %5, %15\n\t"
+      "ds_read_b128 %6, %16\n\t"
+      "ds_read_b128 %7, %17\n\t"
+      "ds_read_b128 %8, %18\n\t"
+      "ds_read_b128 %9, %19\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7]), "v"(ad[8]), "v"(ad[9])
+      : "memory");
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int j = 0; j < MCW; ++j) out[h2][j] = __builtin_bit_cast(bf16x8_t, r[h2 * MCW + j]);
+}
+
+// Workgroup barrier for LDS data only.  __syncthreads() would also wait for
+// every outstanding vector-memory operation, i.e. for the direct loads of
+// the next tile that were just issued; these waits cover only this wave's
+// LDS accesses, and the tile loads are awaited explicitly where a tile is
+// used.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 #ifndef SS_MLA_WAVES_PER_EU
 #define SS_MLA_WAVES_PER_EU 2
@@ -46,12 +164,19 @@ __global__ __launch_bounds__(MNT) __attribute__((amdgpu_waves_per_eu(SS_MLA_WAVE
 decode_mla_kernel(DecodeArgs a) {
   using MM = Mma<bf16_t>;
   using frag = MM::frag;
-  __shared__ __attribute__((aligned(16))) char lat[MTS * MLROW];
-  __shared__ __attribute__((aligned(16))) f32x4_t sx[MW][2][64];
-  __shared__ double csn[2 * ROPE_MAX_PAIRS];
-  __shared__ __attribute__((aligned(16))) bf16_t knew[MD];
-  __shared__ __attribute__((aligned(16))) bf16_t kraw[MD];
-  __shared__ int sh_ticket;
+  // 80 KB in all: the two-tile ring and the partial-score exchange, as one
+  // LDS object (with two, the compiler waits for every direct load before
+  // each read of the other object).  The prologue's raw k_new row and rotary
+  // cos/sin live in the exchange area (unused until the loop), the ticket in
+  // the ring (unused after it).
+  constexpr int SXB = MW * 2 * 64 * 16;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * MTB + SXB];
+  char* ring = lds;
+  f32x4_t(*sx)[2][64] = reinterpret_cast<f32x4_t(*)[2][64]>(lds + 2 * MTB);
+  static_assert(MD * 2 + 2 * ROPE_MAX_PAIRS * 8 <= SXB, "prologue staging");
+  bf16_t* kraw = reinterpret_cast<bf16_t*>(lds + 2 * MTB);
+  double* csn = reinterpret_cast<double*>(lds + 2 * MTB + MD * 2);
+  int* sh_ticket = reinterpret_cast<int*>(ring);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Grid (latent head, row, split), split slowest, as in decode_kernel:
@@ -68,16 +193,25 @@ decode_mla_kernel(DecodeArgs a) {
   const int s0 = split * a.split;
 
   const bf16_t* lb = static_cast<const bf16_t*>(a.kc) + gh * a.C * MD;
-  u32x4_t pre[MLD];
-  // tile [t0, t0 + 32) into registers (streaming hint); rows at or past `hi`
-  // read row hi - 1
-  auto load_tile = [&](int t0, int hi) __attribute__((always_inline)) {
+  // tile [t0, t0 + 32) into ring half `dst` (streaming hint); rows at or past
+  // `hi` read row hi - 1.  Load k of wave w covers LDS units 64 (w + MW k)
+  // .. + 63 of the tile; a lane's tile row and source unit do not depend on
+  // the tile, so they are computed once.
+  int lrow[MLW], lsrc[MLW];
 #pragma unroll
-    for (int i = 0; i < MLD; ++i) {
-      const int id = i * MNT + tid;
-      const int s = min(t0 + id / MCH, hi - 1);
-      pre[i] = ld_stream(reinterpret_cast<const char*>(lb + static_cast<size_t>(s) * MD) +
-                         (id % MCH) * 16);
+  for (int k = 0; k < MLW; ++k) {
+    const int p = (wave + MW * k) * 64 + lane;
+    lrow[k] = p / MCH;
+    lsrc[k] = ((p % MCH) ^ (lrow[k] & 7)) * 16;
+  }
+  const char* lbb = reinterpret_cast<const char*>(lb);
+  auto issue_tile = [&](char* dst, int t0, int hi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < MLW; ++k) {
+      const int srow = min(t0 + lrow[k], hi - 1);
+      __builtin_amdgcn_global_load_lds(
+          (gptr_t)(lbb + static_cast<size_t>(srow) * MROW + lsrc[k]),
+          (lptr_t)(dst + (wave + MW * k) * 1024), 16, 0, CPOL_NT);
     }
   };
 
@@ -134,7 +268,7 @@ decode_mla_kernel(DecodeArgs a) {
   const int ns = cdiv(n_valid, a.split);
   if (split >= ns) return;
   const int s1 = min(s0 + a.split, n_valid);
-  load_tile(s0, s1);  // the first tile, in flight during the rotary work
+  issue_tile(ring, s0, s1);  // the first tile, in flight during the rotary work
   const int SK = a.S + a.K;
   const int slot = p < SK ? p : SK + (p - SK) % a.R;
   const bool own = slot >= s0 && slot < s1;
@@ -156,13 +290,21 @@ decode_mla_kernel(DecodeArgs a) {
     csn[half + i] = sv;
   }
   __syncthreads();
+  // the rotated new row: thread tid < MCH keeps its 16 bytes (8 dims) in
+  // registers, to patch them into the tile that holds the slot
+  u32x4_t knew_v = u32x4_t{0u, 0u, 0u, 0u};
   if (own) {
-    bf16_t* kdst = static_cast<bf16_t*>(a.kc) + (gh * a.C + slot) * MD;
-    for (int d = tid; d < MD; d += MNT) {
-      const bf16_t kv = rotate_pair<bf16_t, bf16_t>(kraw[d], kraw[partner(d)], d, rope, rb, half,
-                                                    csn, csn + half);
-      knew[d] = kv;
-      kdst[d] = kv;
+    if (tid < MCH) {
+      bf16_t e[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int d = 8 * tid + q;
+        e[q] = rotate_pair<bf16_t, bf16_t>(kraw[d], kraw[partner(d)], d, rope, rb, half, csn,
+                                           csn + half);
+      }
+      knew_v = __builtin_bit_cast(u32x4_t, pack_bf16x8(e));
+      *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(a.kc) + (gh * a.C + slot) * MD + 8 * tid) =
+          knew_v;
     }
     if (tid == 0) {
       a.slot_pos[gh * a.C + slot] = p;
@@ -199,38 +341,41 @@ decode_mla_kernel(DecodeArgs a) {
   for (int db = 0; db < MNDB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t0 = s0; t0 < s1; t0 += MTS) {
-    __syncthreads();  // the previous tile is no longer read; knew is visible
-    // the new token: a tile row whose (clamped) slot is `slot` takes it from
-    // LDS, never from the cache memory this launch just wrote; the thread that
-    // stores a chunk also decides its source, so no two stores race
-    const bool patch = own && slot >= t0 && slot < t0 + MTS;
-#pragma unroll
-    for (int i = 0; i < MLD; ++i) {
-      const int id = i * MNT + tid;
-      const int r = id / MCH, c = id % MCH;
-      u32x4_t v = pre[i];
-      if (patch && min(t0 + r, s1 - 1) == slot) v = reinterpret_cast<const u32x4_t*>(knew)[c];
-      *reinterpret_cast<u32x4_t*>(lat + r * MLROW + c * 16) = v;
+  for (int t0 = s0, it = 0; t0 < s1; t0 += MTS, ++it) {
+    char* cur = ring + (it & 1) * MTB;
+    // this wave's direct loads of the tile have landed; after the barrier
+    // the whole tile is in LDS and every wave is done with the previous one
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the next tile streams into the other half during this one
+    if (t0 + MTS < s1) issue_tile(ring + ((it + 1) & 1) * MTB, t0 + MTS, s1);
+    if (own && slot >= t0 && slot < t0 + MTS) {
+      // (uniform) the new token: every tile row whose (clamped) slot is
+      // `slot` takes it from registers, never from the cache memory this
+      // launch wrote
+      if (tid < MCH)
+        for (int r = slot - t0; r < MTS; ++r)
+          if (min(t0 + r, s1 - 1) == slot)
+            *reinterpret_cast<u32x4_t*>(cur + lat_byte(r, tid)) = knew_v;
+      lds_barrier();
     }
-    __syncthreads();  // tile visible
-    if (t0 + MTS < s1) load_tile(t0 + MTS, s1);  // next tile in flight during this one
 
+    // all of this wave's K fragments first, then the MFMAs: one LDS round
+    // trip (chunks past the wave's range have zero queries and add nothing;
+    // their reads stay inside the row)
+    frag kfr[2][MCW];
+    kfrags(cur, koff, clo, qg, kfr);
     f32x4_t sacc[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       sacc[h2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const char* row = lat + (16 * h2 + koff) * MLROW + qg * 16;
 #pragma unroll
-      for (int j = 0; j < MCW; ++j)
-        if (clo + j < chi) {
-          const frag kfr = MM::load(reinterpret_cast<const bf16_t*>(row + (clo + j) * 64));
-          sacc[h2] = MM::mma(kfr, qf[0][j], sacc[h2]);
-          sacc[h2] = MM::mma(kfr, qf[1][j], sacc[h2]);
-        }
+      for (int j = 0; j < MCW; ++j) {
+        sacc[h2] = MM::mma(kfr[h2][j], qf[0][j], sacc[h2]);
+        sacc[h2] = MM::mma(kfr[h2][j], qf[1][j], sacc[h2]);
+      }
       sx[wave][h2][lane] = sacc[h2];
     }
-    __syncthreads();  // partial scores visible
+    lds_barrier();  // partial scores visible
     float x[8];
     float tmax = -INFINITY;
 #pragma unroll
@@ -245,27 +390,34 @@ decode_mla_kernel(DecodeArgs a) {
         tmax = fmaxf(tmax, x[i]);
       }
     }
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
+    tmax = max_across_16(tmax);
+    tmax = max_across_32(tmax);
     const float mnew = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - mnew);
+    const float alpha = fast_exp2(m_run - mnew);
     m_run = mnew;
     float pf[8];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pf[i] = exp2f(x[i] - mnew);
+      pf[i] = fast_exp2(x[i] - mnew);
       psum += pf[i];
     }
     l_run = l_run * alpha + psum;
     frag pfr[2];
     Split<bf16_t>::make(pf, pfr);
+    // V fragments in batches of VB (VB reads in flight per round trip)
+    constexpr int VB = 4;
+    static_assert(MNDB % VB == 0, "value-block batches");
 #pragma unroll
-    for (int db = 0; db < MNDB; ++db) {
-      oacc[db] *= alpha;
-      const frag vfr = PvOps<bf16_t>::vfrag(lat, MLROW, MNDB * wave + db, col, qg, 0);
-      oacc[db] = MM::mma(vfr, pfr[0], oacc[db]);
-      oacc[db] = MM::mma(vfr, pfr[1], oacc[db]);
+    for (int d0 = 0; d0 < MNDB; d0 += VB) {
+      frag vfr[VB];
+      vfrags<VB>(cur, MNDB * wave + d0, lane, vfr);
+#pragma unroll
+      for (int q = 0; q < VB; ++q) {
+        oacc[d0 + q] *= alpha;
+        oacc[d0 + q] = MM::mma(vfr[q], pfr[0], oacc[d0 + q]);
+        oacc[d0 + q] = MM::mma(vfr[q], pfr[1], oacc[d0 + q]);
+      }
     }
   }
   l_run = xor_sum(l_run, 16);
@@ -286,10 +438,10 @@ decode_mla_kernel(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();                // ... and every other thread's
   if (tid == 0)
-    sh_ticket = __hip_atomic_fetch_add(a.counter + gh, 1, __ATOMIC_RELAXED,
+    *sh_ticket = __hip_atomic_fetch_add(a.counter + gh, 1, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (sh_ticket != ns - 1) return;
+  if (*sh_ticket != ns - 1) return;
   merge_splits<bf16_t, MDV, 4>(a, head0, G, ns, tid, MNT);
   if (tid == 0) a.counter[gh] = 0;  // ready for the next call
 }
