@@ -276,16 +276,16 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
       x[i] = s < w1 ? sacc[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, x[i]);
     }
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
+    tmax = max_across_16(tmax);
+    tmax = max_across_32(tmax);
     const float mnew = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - mnew);
+    const float alpha = fast_exp2(m_run - mnew);
     m_run = mnew;
     float pf[8];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pf[i] = exp2f(x[i] - mnew);
+      pf[i] = fast_exp2(x[i] - mnew);
       psum += pf[i];
     }
     l_run = l_run * alpha + psum;

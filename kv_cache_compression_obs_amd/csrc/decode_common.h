@@ -58,15 +58,24 @@ __device__ __forceinline__ u32x4_t ld_stream(const void* p) {
 // the Q.K^T accumulator left that slot's probability (see decode_kernel).
 template <typename T> struct PvOps;
 
+// bf16: two transposing LDS reads (gfx950 ds_read_b64_tr_b16) build the
+// fragment.  Within each group of 16 lanes, lane 4a + b receives element b
+// of the 8-byte chunks that lanes a + 4k (k < 4) address; so lane (col, qg)
+// addresses dims 16 db + 4 (col % 4) .. + 3 of slot 4 (col / 4) + qg
+// (elements i < 4) and of slot 16 + 4 (col / 4) + qg (i >= 4), and receives
+// dim 16 db + col of slots 4 i + qg.  lrow must be a multiple of 8 bytes.
 template <> struct PvOps<bf16_t> {
   static constexpr int STEPS = 1;
   static __device__ __forceinline__ bf16x8_t vfrag(const char* vt, int lrow, int db, int col,
                                                    int qg, int) {
-    bf16_t e[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      e[i] = *reinterpret_cast<const bf16_t*>(vt + (4 * i + qg) * lrow + (16 * db + col) * 2);
-    return pack_bf16x8(e);
+    typedef short v4i16_t __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v4i16_t* lds_v4;
+    const char* base = vt + (4 * (col >> 2) + qg) * lrow + (16 * db + 4 * (col & 3)) * 2;
+    const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)base));
+    const u32x2_t hi =
+        __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(base + 16 * lrow)));
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
   }
 };
 
