@@ -123,6 +123,20 @@ def score_key_bytes(w, elem):
     return w["B"] * w["n_kv_heads"] * (w["L"] + m) * w["d_qk"] * elem
 
 
+def decode_kernel_name(w):
+    """The kernel the library runs for this workload's decode step: the
+    latent kernel for MLA, the direct-load ring kernel for bf16 K/V caches
+    whose rotary range is empty or starts and splits on multiples of 8 dims,
+    the register-tile kernel otherwise."""
+    if w["v_aliases_k"]:
+        return "decode_mla_kernel"
+    half = (w["rope_end"] - w["rope_begin"]) // 2 if w["rope_theta"] > 0 else 0
+    aligned = half == 0 or (w["rope_begin"] % 8 == 0 and half % 8 == 0)
+    if w["dtype"] == "bf16" and w["d_qk"] == w["d_v"] and w["d_qk"] in (64, 128) and aligned:
+        return "decode_ring_kernel"
+    return "decode_kernel"
+
+
 def committed_profile(workload):
     """The committed rocprofv3 record of the decode kernel on this workload
     (HBM bytes per launch from FETCH_SIZE/WRITE_SIZE, average launch duration
@@ -463,8 +477,7 @@ def run_steps(ss, torch, synth, hip, w, steps, warmup, n_dec, R, inp=None, dec=N
     score_s = sum(score_ms) / len(score_ms) / 1e3
     achieved = dec_b / attn_avg_s / 1e9
     roof = {
-        "kernel": ("decode_mla_kernel" if w["v_aliases_k"] else "decode_kernel")
-        + " (RoPE + ring scatter + split-C flash-decode + merge)",
+        "kernel": decode_kernel_name(w) + " (RoPE + ring scatter + split-C flash-decode + merge)",
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,

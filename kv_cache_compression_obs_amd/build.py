@@ -27,7 +27,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["api.cpp", "decode.hip", "decode_mla.hip", "prefill.hip", "score.hip", "select.hip"]
+SOURCES = ["api.cpp", "decode.hip", "decode_mla.hip", "decode_ring.hip", "prefill.hip", "score.hip", "select.hip"]
 
 
 def _compile(src: str, extra=(), build_dir=BUILD) -> str:

@@ -379,6 +379,13 @@ hipError_t launch_decode(int dtype, int D, int DV, int alias, const DecodeArgs& 
   if (dtype == 0 && D == 64 && DV == 64) return run_decode<float, 64, 64>(a, st, ev0, ev1);
   if (dtype == 0 && D == 128 && DV == 128)
     return run_decode<float, 128, 128>(a, st, ev0, ev1);
+#if SS_DECODE_RING
+  // (its rotation takes 8 aligned dims at a time: the rotary range must start
+  // and split on multiples of 8 dims)
+  if (dtype == 1 && D == DV && (D == 64 || D == 128) &&
+      (a.rope_half == 0 || (a.rope_begin % 8 == 0 && a.rope_half % 8 == 0)))
+    return launch_decode_ring(D, a, st, ev0, ev1);
+#endif
   if (dtype == 1 && D == 64 && DV == 64) return run_decode<bf16_t, 64, 64>(a, st, ev0, ev1);
   if (dtype == 1 && D == 128 && DV == 128)
     return run_decode<bf16_t, 128, 128>(a, st, ev0, ev1);

@@ -86,6 +86,9 @@ hipError_t launch_prefill_scores(int dtype, int D, const PrefillArgs& a, hipStre
                                  hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_decode_mla(int dtype, int D, int DV, const DecodeArgs& a, hipStream_t st,
                              hipEvent_t ev0, hipEvent_t ev1);
+// bf16 K/V caches of D = DV = 64 or 128 dims (decode_ring.hip).
+hipError_t launch_decode_ring(int D, const DecodeArgs& a, hipStream_t st, hipEvent_t ev0,
+                              hipEvent_t ev1);
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t st);
 
 // The library's own decode scratch for callers that cannot allocate: a
@@ -125,6 +128,11 @@ constexpr int DECODE_WAVES = 4;   // waves per decode workgroup
 #endif
 constexpr int MLA_TARGET_WG = SS_MLA_TARGET_WG;
 constexpr int MLA_MAX_TILES = SS_MLA_MAX_TILES;
+// bf16 K/V decode through the direct-load LDS ring (decode_ring.hip); 0 keeps
+// it on decode_kernel (register tiles), as fp32 caches are.
+#ifndef SS_DECODE_RING
+#define SS_DECODE_RING 1
+#endif
 constexpr int DECODE_TARGET_WAVES = SS_DECODE_TARGET_WAVES;
 constexpr int DECODE_MAX_TILES = SS_DECODE_MAX_TILES;
 // LDS row stride of the decode V tile (bytes) for value rows of `row_bytes`

@@ -49,6 +49,50 @@ def test_decode_bf16_rope_ring(d):
     decode_case(w, L=200, steps=150, seed=5, check_every=5)
 
 
+@pytest.mark.parametrize("rope", [(32, 96), (2, 66), (0, 0)],
+                         ids=["aligned_partial", "unaligned", "none"])
+def test_decode_bf16_rope_ranges(rope):
+    # bf16 caches decode through the direct-load ring kernel when the rotary
+    # range starts and splits on multiples of 8 dims (or is empty); other
+    # ranges take the register-tile kernel.  Both must match the oracle.
+    b, e = rope
+    w = synth.workload("llama8b_c4k", B=2, rope_begin=b, rope_end=e,
+                       rope_theta=500000.0 if e > b else 0.0, L_sink=4, K=28, L_recent=64)
+    say(f"decode bf16 rope [{b}, {e}) C=96 L=200 steps=40")
+    decode_case(w, L=200, steps=40, seed=11, check_every=3)
+
+
+@pytest.mark.parametrize("g", [1, 16])
+def test_decode_bf16_group_sizes(g):
+    # one q-head per kv-head, and the largest group (16 q-heads)
+    w = synth.workload("llama8b_c4k", B=2, n_q_heads=2 * g, n_kv_heads=2, W=16, L_sink=4,
+                       K=60, L_recent=200)
+    say(f"decode bf16 G={g} C=264 L=500 steps=30")
+    decode_case(w, L=500, steps=30, seed=12, check_every=4)
+
+
+def test_decode_bf16_mixed_rows_inactive_and_mismatch():
+    # the mixed-rows case on bf16 caches: an inactive row (pos < 0), a row
+    # whose pos jumps ahead of n_tokens once (error flag, step applied at
+    # pos), every row crossing C = 96 during the run
+    w = synth.workload("llama8b_c4k", B=4, L_sink=4, K=28, L_recent=64)
+    L = 90
+    base = np.array([L, L, L, L])
+
+    def positions(t):
+        p = base + t
+        if t < 4:
+            p[2] = -1
+        else:
+            p[2] = L + t - 4
+        if t >= 6:
+            p[3] = L + t + 2
+        return p
+
+    say("decode bf16 mixed rows C=96")
+    decode_case(w, L=L, steps=14, seed=13, positions=positions)
+
+
 def test_decode_fp32_d128_rope():
     w = synth.workload("llama8b_c4k", B=2, dtype="f32", L_sink=4, K=28, L_recent=64)
     say("decode f32 d=128 C=96 L=300 steps=70")
