@@ -77,59 +77,6 @@ template <int D> struct Ring {
   static __device__ __forceinline__ int byte(int r, int u) { return (r * RU + (u ^ swz(r))) * 16; }
 };
 
-__device__ __forceinline__ int lds_addr(const char* p) {
-  return static_cast<int>((uintptr_t)((const __attribute__((address_space(3))) char*)p));
-}
-
-// N 16-byte LDS reads in one asm block that also waits for them (the
-// compiler, which cannot tell LDS reads from the direct loads still writing
-// the ring, would otherwise wait for every outstanding vector-memory load).
-template <int N>
-__device__ __forceinline__ void lds_read16(const int (&ad)[N], u32x4_t (&r)[N]) {
-  if constexpr (N == 8) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %10\n\t"
-        "ds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %13\n\t"
-        "ds_read_b128 %6, %14\n\t"
-        "ds_read_b128 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-          "=&v"(r[6]), "=&v"(r[7])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
-          "v"(ad[7])
-        : "memory");
-  } else if constexpr (N == 4) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
-        : "memory");
-  } else {
-    static_assert(N == 2, "2, 4 or 8 reads");
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %3\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1])
-        : "v"(ad[0]), "v"(ad[1])
-        : "memory");
-  }
-}
-
-// 16-byte LDS store, for the same reason (its completion is awaited by the
-// next lds_barrier or asm wait).
-__device__ __forceinline__ void lds_write16(int ad, u32x4_t v) {
-  asm volatile("ds_write_b128 %0, %1" : : "v"(ad), "v"(v) : "memory");
-}
-
 // K fragments (A operands of S^T = K . Q^T) of a wave: lane (m, g) takes
 // dims 32 c + 8 g .. + 7 of tile row `row` (= 16 w + m), c < NC.
 template <int D>
@@ -142,18 +89,6 @@ __device__ __forceinline__ void kfrags(const char* kt, int row, int g, bf16x8_t 
   lds_read16<RG::NC>(ad, r);
 #pragma unroll
   for (int c = 0; c < RG::NC; ++c) out[c] = __builtin_bit_cast(bf16x8_t, r[c]);
-}
-
-// Rotate-half rotary embedding of one dim from the stored value x and its
-// partner xp, in fp64, rounded once to O: upper = the dim lies in the second
-// half of the rotary range; c, s = cos, sin of the pair's angle.  Outside the
-// range the value passes through.
-template <typename O>
-__device__ __forceinline__ O rot_dim(bf16_t x, bf16_t xp, bool in, bool upper, double c, double s) {
-  if (!in) return from_f32<O>(bf16_to_f32(x));
-  const double v = bf16_to_f32(x), w = bf16_to_f32(xp);
-  if (!upper) return from_f64<O>(v * c - w * s);
-  return from_f64<O>(v * c + w * s);
 }
 
 // Four V^T fragments (A operands of the 16-slot P.V contraction), value
@@ -184,12 +119,6 @@ __device__ __forceinline__ void vfrags4(const char* vt, int wrow, int lane, int 
       : "memory");
 #pragma unroll
   for (int q = 0; q < 4; ++q) out[q] = __builtin_bit_cast(s16x4_t, r[q]);
-}
-
-// Workgroup barrier for LDS data only (__syncthreads() would also wait for the
-// direct loads of the next tile, just issued).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ f32x4_t mma16(s16x4_t a, s16x4_t b, f32x4_t c) {
