@@ -268,9 +268,8 @@ decode_mla_kernel(DecodeArgs a) {
     const int k = krot + i;
     return s0 + (k < ntile ? k : k - ntile) * MTS;
   };
-  // the first two tiles, in flight during the rotary work
+  // the first tile, in flight during the rotary work
   issue_tile(ring, tile_at(0), s1);
-  if (ntile > 1) issue_tile(ring + MTB, tile_at(1), s1);
   const int SK = a.S + a.K;
   const int slot = p < SK ? p : SK + (p - SK) % a.R;
   const bool own = slot >= s0 && slot < s1;
@@ -342,6 +341,11 @@ decode_mla_kernel(DecodeArgs a) {
     qf[1][j] = parts[1];
   }
 
+  // the second tile once the rotary work is done: issued right behind the
+  // first, its loads stalled the wave until queue space freed, i.e. until
+  // the first tile's data was coming back, and the rotary work waited with
+  // them (193.5 against 195.3 us per launch)
+  if (ntile > 1) issue_tile(ring + MTB, tile_at(1), s1);
   // ------------------------------------------------------------ main loop
   const int koff = 4 * (col & 3) + (col >> 2);
   f32x4_t oacc[MNDB];
@@ -354,16 +358,13 @@ decode_mla_kernel(DecodeArgs a) {
     char* cur = ring + (it & 1) * MTB;
     // this wave's direct loads of the tile have landed; after the barrier
     // the whole tile is in LDS and every wave is done with the previous one
-    // (this wave issues no vector-memory operation but the direct loads until
-    // the loop ends, so vmcnt counts tiles: in the first iteration the second
-    // tile may still be in flight)
+    // (this wave issues no vector-memory operation but the direct loads
+    // between the first tile and the end of the loop, so vmcnt counts tiles:
+    // in the first iteration the second tile may still be in flight)
     if (it == 0 && ntile > 1)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(MLW) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // from the second iteration on, the next tile streams into the other
-    // half during this one (the first two were issued in the prologue)
-    if (it > 0 && it + 1 < ntile) issue_tile(ring + ((it + 1) & 1) * MTB, tile_at(it + 1), s1);
     if (own && slot >= t0 && slot < t0 + MTS) {
       // (uniform) the new token: every tile row whose (clamped) slot is
       // `slot` takes it from registers, never from the cache memory this
@@ -428,6 +429,15 @@ decode_mla_kernel(DecodeArgs a) {
     for (int d0 = 0; d0 < MNDB; d0 += VB) {
       frag vfr[VB];
       vfrags<VB>(cur, MNDB * wave + d0, lane, vfr);
+      // From the second iteration on, the next tile streams into the other
+      // half from here (the first two were issued before the loop).  Where
+      // in the iteration its loads go out matters: measured per launch,
+      // right after the barrier 193.1 us, after the K fragment reads 191.8,
+      // after the score exchange 191.1, after the softmax 190.6, here (after
+      // the first value-fragment batch) 189.5, after the second 204.6, at
+      // the end of the iteration 202.0.
+      if (d0 == 0 && it > 0 && it + 1 < ntile)
+        issue_tile(ring + ((it + 1) & 1) * MTB, tile_at(it + 1), s1);
 #pragma unroll
       for (int q = 0; q < VB; ++q) {
         oacc[d0 + q] *= alpha;

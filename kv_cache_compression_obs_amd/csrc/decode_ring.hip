@@ -25,8 +25,8 @@
 //
 // Prologue: each thread rotates one 16-byte unit (8 dims) of the G queries
 // and, below RU, of the new k row (fp64 angles; the rotary table and the
-// rotated queries pass through LDS behind the ring) while the first two tiles
-// stream in.  The workgroup whose split holds the ring slot of pos patches the
+// rotated queries pass through LDS behind the ring) while the first tile
+// streams in; the second is issued after that work.  The workgroup whose split holds the ring slot of pos patches the
 // rotated key and the value from registers into the tile that holds the slot
 // (nothing reads back what this launch writes to HBM), and once its loop is
 // done writes them into that slot (evicting pos - L_recent), sets slot_pos
@@ -206,8 +206,8 @@ __global__ __launch_bounds__(RNT) void decode_ring_kernel(DecodeArgs a) {
   // rows (8 dims) and the 8 dims it pairs with under the rotation; the same
   // for the new k row (threads < RU: unit tid) and the new v unit; the rotary
   // frequency of pair tid; the row's token count.  Then (once pos has given
-  // the split's valid end) the first two tiles, whose latency covers the
-  // rotary work.  The rotary range starts and splits
+  // the split's valid end) the first tile, whose latency covers the rotary
+  // work.  The rotary range starts and splits
   // on multiples of 8 dims (checked on the host), so the 8 partners of 8
   // aligned dims are 8 aligned consecutive dims; outside the range the
   // partner load reads the neighbouring 8 dims of the row, unused.
@@ -250,9 +250,8 @@ __global__ __launch_bounds__(RNT) void decode_ring_kernel(DecodeArgs a) {
   // compiler cannot count direct loads together with ordinary ones, so a
   // value loaded before them and used after would wait for the whole tile.
   asm volatile("" : : "v"(qv), "v"(qpv), "v"(kv), "v"(kpv), "v"(vld), "v"(ang) : "memory");
-  // the first two tiles, in flight during the rotary work
+  // the first tile, in flight during the rotary work
   issue_tile(lds, s0, s1);
-  if (s0 + RTS < s1) issue_tile(lds + 2 * TB, s0 + RTS, s1);
   const int SK = a.S + a.K;
   const int slot = p < SK ? p : SK + (p - SK) % a.R;
   const bool own = slot >= s0 && slot < s1;
@@ -342,6 +341,10 @@ __global__ __launch_bounds__(RNT) void decode_ring_kernel(DecodeArgs a) {
     }
   }
 
+  // the second tile once the rotary work is done (issued right behind the
+  // first, its loads stalled the wave until queue space freed: 46.5 against
+  // 47.2 us per launch at 16 x 8 x 4096 slots)
+  if (s0 + RTS < s1) issue_tile(lds + 2 * TB, s0 + RTS, s1);
   // ------------------------------------------------------------ main loop
   const int wrow = 16 * wave;  // this wave's tile rows
   f32x4_t oacc[NDB];
@@ -354,15 +357,15 @@ __global__ __launch_bounds__(RNT) void decode_ring_kernel(DecodeArgs a) {
     // this wave's direct loads of the tile have landed (and its reads of the
     // previous tile, and of the staged queries, are done); after the barrier
     // the whole tile is in LDS and every wave is done with the other half
-    // (this wave issues no vector-memory operation but the direct loads until
-    // the loop ends, so vmcnt counts tiles: in the first iteration the
-    // second tile may still be in flight)
+    // (this wave issues no vector-memory operation but the direct loads
+    // between the first tile and the end of the loop, so vmcnt counts tiles:
+    // in the first iteration the second tile may still be in flight)
     if (it == 0 && t0 + RTS < s1)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(LW) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // from the second iteration on, the next tile streams into the other
-    // half during this one (the first two were issued in the prologue)
+    // half during this one (the first two were issued before the loop)
     if (it > 0 && t0 + RTS < s1) issue_tile(lds + ((it + 1) & 1) * 2 * TB, t0 + RTS, s1);
     if (own && slot >= t0 && slot < t0 + RTS) {
       // (uniform) the new token: every tile row whose (clamped) slot is
