@@ -137,20 +137,30 @@ def decode_kernel_name(w):
     return "decode_kernel"
 
 
+def source_digest(paths):
+    """sha256 over the code of the given sources with comments and blank
+    space removed (an edit to a comment leaves a kernel's record valid)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in paths:
+        text = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def committed_profile(workload):
     """The committed rocprofv3 record of the decode kernel on this workload
     (HBM bytes per launch from FETCH_SIZE/WRITE_SIZE, average launch duration
     from --kernel-trace --stats), or None if there is none or the kernel
     sources changed since it was taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in rec["sources"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    return rec if h.hexdigest() == rec["source_sha256"] else None
+    return rec if source_digest(rec["sources"]) == rec["source_digest"] else None
 
 
 def cpu_baseline(w, inp, dec, budget_s=15.0):
