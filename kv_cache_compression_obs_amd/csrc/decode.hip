@@ -354,7 +354,7 @@ __global__ __launch_bounds__(64 * DW) void decode_kernel(DecodeArgs a) {
                                        __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sh_ticket != ns - 1) return;
-  merge_splits<T, DV, 1>(a, head0, G, ns, tid, 64 * DW);
+  merge_splits<T, DV>(a, head0, G, ns, tid, 64 * DW);
   if (tid == 0) a.counter[gh] = 0;  // ready for the next call
 }
 

@@ -201,20 +201,97 @@ __device__ __forceinline__ void wave_sync() {
 // Ordering: every writer waits for its partial stores to complete at the
 // device-coherent level before it takes its ticket; the merging workgroup
 // holds the last ticket, so all partials are there before it issues its
-// device-scope loads (ld_dev).  No acquire fence is used: a fence would
+// device-scope loads (ld_dev, ld_dev4).  No acquire fence is used: a fence would
 // invalidate this XCD's whole L2 and slow every workgroup still streaming on
 // it.  This rests on the gfx942/gfx950 cache policy rather than on the HIP
 // memory model's release/acquire pair: sc1 stores (agent-scope atomic stores
 // and st_dev4) write through the XCD's L2, s_waitcnt vmcnt(0) returns once
 // they are acknowledged at the device-coherent level, and sc1 loads
-// (agent-scope atomic loads and ld_dev4) never hit a stale line of this XCD's
-// L2.  Checked with the ROCm 7.2 toolchain; the determinism, many-split and
+// (agent-scope atomic loads and ld_dev4) never hit a stale line of this
+// XCD's L2.  Checked with the ROCm 7.2 toolchain; the determinism, many-split and
 // graph-replay decode tests guard it.  The merge computes
 //   out[head, dv] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
 // in split order.
-template <typename T, int DV, int NI>
+template <typename T, int DV, int NI, int MB>
+__device__ __forceinline__ void merge_splits_mb(const DecodeArgs& a, size_t head0, int G, int ns,
+                                                int tid, int nthreads) {
+  // Each thread merges NI outputs of one head (4 dims each, NO = DV/4/NI
+  // apart so that every load instruction stays coalesced; they share the
+  // splits' (m, l)) at once, MB splits per batch: one memory round trip per
+  // batch.  Loads are unconditional (a split index
+  // past ns rereads the last split), so no wait is forced between them; the
+  // surplus gets weight 0.
+  static_assert((DV / 4) % NI == 0, "an output group stays within one head");
+  constexpr int NO = DV / 4 / NI;
+  const int ngrp = G * NO;
+  for (int q = tid; q < ngrp; q += nthreads) {
+    const int g = q / NO, d40 = q % NO;
+    const size_t base = (head0 + g) * a.n_split;
+    const __amdgpu_buffer_rsrc_t ob = dev_buffer(a.part_o + base * DV, a.n_split * DV * 4);
+    float M = -INFINITY, L = 0.f;
+    f32x4_t acc[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < ns; sb += MB) {
+      float mv[MB], lv[MB];
+      f32x4_t ov[MB][NI];
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int sp = min(sb + j, ns - 1);
+        mv[j] = ld_dev(a.part_ml + 2 * (base + sp));
+        lv[j] = ld_dev(a.part_ml + 2 * (base + sp) + 1);
+#pragma unroll
+        for (int k = 0; k < NI; ++k) ov[j][k] = ld_dev4(ob, (sp * DV + 4 * (d40 + k * NO)) * 4);
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        if (sb + j < ns) Mn = fmaxf(Mn, mv[j]);
+      // a batch of splits without slots leaves Mn at -inf: nothing to add
+      const float Mr = Mn == -INFINITY ? 0.f : Mn;
+      const float r = exp2f(M - Mr);
+      L *= r;
+#pragma unroll
+      for (int k = 0; k < NI; ++k) acc[k] *= r;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const float w = sb + j < ns ? exp2f(mv[j] - Mr) : 0.f;
+        L += w * lv[j];
+#pragma unroll
+        for (int k = 0; k < NI; ++k) acc[k] += w * ov[j][k];
+      }
+      M = Mn;
+    }
+    const float inv = 1.f / L;
+    T* o = static_cast<T*>(a.out) + (head0 + g) * DV + 4 * d40;
+#pragma unroll
+    for (int k = 0; k < NI; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[4 * k * NO + e] = from_f32<T>(acc[k][e] * inv);
+  }
+}
+
+// Batches of 4 splits when there are at most 4, of 8 up to 8, else of 16 (a
+// batch rereads the last split up to its size: at 4 splits, 48 loads per
+// thread where 12 do; llama8b_c4k 46.5 -> 45.4 us per launch, llama8b_128k
+// 158.9 -> 158.2 us).
+template <typename T, int DV>
 __device__ __forceinline__ void merge_splits(const DecodeArgs& a, size_t head0, int G, int ns,
                                              int tid, int nthreads) {
+  if (ns <= 4) {
+    merge_splits_mb<T, DV, 1, 4>(a, head0, G, ns, tid, nthreads);
+  } else if (ns <= 8) {
+    merge_splits_mb<T, DV, 1, 8>(a, head0, G, ns, tid, nthreads);
+  } else {
+    merge_splits_mb<T, DV, 1, 16>(a, head0, G, ns, tid, nthreads);
+  }
+}
+
+template <typename T, int DV, int NI>
+__device__ __forceinline__ void merge_splits_wide(const DecodeArgs& a, size_t head0, int G, int ns,
+                                             int tid, int nthreads) {
+  // (the latent kernel's merge: 8 heads x 512 dims of 16 splits; its (m, l)
+  // as two 4-byte loads, which measured faster there than one 8-byte load)
   // Each thread merges NI outputs of one head (4 dims each, NO = DV/4/NI
   // apart so that every load instruction stays coalesced; they share the
   // splits' (m, l)) at once, MB splits per batch: one memory round trip per

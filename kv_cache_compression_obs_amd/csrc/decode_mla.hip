@@ -493,7 +493,7 @@ decode_mla_kernel(DecodeArgs a) {
                                        __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (*sh_ticket != ns - 1) return;
-  merge_splits<bf16_t, MDV, 4>(a, head0, G, ns, tid, MNT);
+  merge_splits_wide<bf16_t, MDV, 4>(a, head0, G, ns, tid, MNT);
   if (tid == 0) a.counter[gh] = 0;  // ready for the next call
 }
 

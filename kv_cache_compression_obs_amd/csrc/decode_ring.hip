@@ -500,7 +500,7 @@ __global__ __launch_bounds__(RNT) void decode_ring_kernel(DecodeArgs a) {
                                        __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (*sh_ticket != ns - 1) return;
-  merge_splits<bf16_t, D, 1>(a, head0, G, ns, tid, RNT);
+  merge_splits<bf16_t, D>(a, head0, G, ns, tid, RNT);
   if (tid == 0) a.counter[gh] = 0;  // ready for the next call
 }
 
