@@ -1,6 +1,10 @@
 // Decode step over the fixed-size cache, as one kernel: rotary embedding of
 // the new token, its ring-buffer scatter, split-C flash-decode attention with
-// GQA head grouping on MFMA, and the merge of the split partials.
+// GQA head grouping on MFMA, and the merge of the split partials.  This
+// register-tile kernel serves fp32 caches and rotary ranges that do not start
+// and split on multiples of 8 dims; bf16 caches otherwise go through the
+// direct-load ring kernel (decode_ring.hip), latent caches through
+// decode_mla.hip.
 //
 // Follows "SnapStream: Taming KV-Cache Eviction for Dataflow Accelerators",
 // sections "Ring Buffer vs. Naive Slicing" (decode rotates only the recent
