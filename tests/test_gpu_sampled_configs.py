@@ -16,8 +16,8 @@ from kv_cache_compression_obs_amd import snapstream as ss
 from kv_cache_compression_obs_amd import synth
 from parity import decode_case, lib_config, prefill_case, say
 
-N_CONFIGS = 24      # K/V heads of 64 or 128 dims
-N_LATENT = 8        # latent rows (576 dims, the value is the first 512)
+N_CONFIGS = 64      # K/V heads of 64 or 128 dims
+N_LATENT = 16        # latent rows (576 dims, the value is the first 512)
 
 
 def sample_config(i):
