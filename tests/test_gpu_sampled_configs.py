@@ -6,7 +6,10 @@ part or none), batch and prompt length (stored as is, or compressed by a
 little or by a lot); and latent (MLA) configurations of 576-dim rows with
 the same spread of sizes.  Each configuration runs the prefill comparison
 (scores, selection, slot map, gathered rows) and a decode run long enough to
-wrap a short ring, against the oracle.
+wrap a short ring, against the oracle.  Most also build a packed batch of
+prompts of drawn lengths (stored and compressed mixed, into drawn cache
+rows, with the log-sum-exp given on every other draw) through
+ss_prefill_compress_varlen, every request checked against the oracle.
 
 The sampler only draws configurations; it computes nothing of the method."""
 import numpy as np
@@ -15,6 +18,7 @@ import pytest
 from kv_cache_compression_obs_amd import snapstream as ss
 from kv_cache_compression_obs_amd import synth
 from parity import decode_case, lib_config, prefill_case, say
+from test_gpu_varlen import _varlen_case
 
 N_CONFIGS = 64      # K/V heads of 64 or 128 dims
 N_LATENT = 16        # latent rows (576 dims, the value is the first 512)
@@ -119,6 +123,11 @@ def test_sampled_configs_are_valid():
         cfg = lib_config(w)
         assert ss.ss_prefill_workspace_bytes(cfg, w["B"], L) > 0, describe(w, L)
         assert ss.ss_decode_workspace_bytes(cfg, w["B"]) > 0, describe(w, L)
+        # the packed batch: lengths >= 1, distinct rows inside the cache
+        _, lens, rows, B_max, _ = varlen_draw(kind, i)
+        assert min(lens) >= 1 and max(lens) > w["C"]
+        assert len(set(rows)) == len(rows) == len(lens) and 0 <= min(rows) and max(rows) < B_max
+        assert ss.ss_prefill_workspace_bytes(cfg, len(lens), max(lens)) > 0
 
 
 @pytest.mark.gpu
@@ -130,3 +139,28 @@ def test_sampled_config(kind, i):
     prefill_case(w, seed, L=L)
     steps = min(w["L_recent"] + 8, 48)
     decode_case(w, L=L, steps=steps, seed=seed + 100, check_every=4)
+
+
+def varlen_draw(kind, i):
+    """Request lengths, cache rows and the lse choice of the packed batch that
+    goes with sampled configuration (kind, i)."""
+    w, _ = config(kind, i)
+    rng = np.random.default_rng((9500 if kind == "kv" else 9700) + i)
+    C = w["C"]
+    lens = [C + int(rng.integers(1, 2500))]  # at least one compressed request
+    for _ in range(int(rng.integers(1, 6))):
+        r = rng.integers(4)
+        lens.append(int(rng.integers(1, C + 1)) if r == 0 else C + 1 if r == 1
+                    else C + int(rng.integers(2, 2500)))
+    B_max = len(lens) + int(rng.integers(0, 3))
+    rows = [int(x) for x in rng.permutation(B_max)[:len(lens)]]
+    return w, lens, rows, B_max, bool(i % 2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind,i", [c for c in CONFIGS if c[0] == "latent" or c[1] < 24])
+def test_sampled_config_varlen(kind, i):
+    w, lens, rows, B_max, given_lse = varlen_draw(kind, i)
+    say(f"sampled {kind} config {i}, varlen: {describe(w, max(lens))}")
+    _varlen_case(w, (60 if kind == "kv" else 80) + i, lens, rows=rows, given_lse=given_lse,
+                 B_max=B_max)
