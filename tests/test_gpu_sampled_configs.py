@@ -95,11 +95,36 @@ def sample_latent_config(i):
     return w, L
 
 
-CONFIGS = ([("kv", i) for i in range(N_CONFIGS)] + [("latent", i) for i in range(N_LATENT)])
+def sample_long_config(i):
+    """(workload, prompt length) of sampled long configuration i: more than
+    16384 middle keys per group, so the selection is split over parts of the
+    group (part boundaries at drawn places, pooling windows across them) and
+    the score passes run over several chunks."""
+    rng = np.random.default_rng(9900 + i)
+    d = [64, 128][rng.integers(2)]
+    Hkv = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 4, 8]))
+    R = int(rng.integers(32, 1024))
+    W = int(rng.integers(1, min(32, R) + 1))
+    S = int(rng.choice([0, 4, 64]))
+    K = int(rng.integers(1, 4000))
+    L = S + R + int(rng.integers(16385, 40000))
+    w = synth.workload(
+        "tiny_fp32", B=1, n_q_heads=G * Hkv, n_kv_heads=Hkv, d_qk=d, d_v=d, L_sink=S, K=K,
+        L_recent=R, W=W, pool=int(rng.choice([1, 7, 31, 63, 255])),
+        dtype=["f32", "bf16"][rng.integers(2)], rope_theta=5e5, rope_begin=0, rope_end=d,
+        heavy_keys=0, key_lognormal=bool(rng.integers(2)))
+    return w, L
+
+
+N_LONG = 8
+CONFIGS = ([("kv", i) for i in range(N_CONFIGS)] + [("latent", i) for i in range(N_LATENT)]
+           + [("long", i) for i in range(N_LONG)])
 
 
 def config(kind, i):
-    return sample_config(i) if kind == "kv" else sample_latent_config(i)
+    return {"kv": sample_config, "latent": sample_latent_config,
+            "long": sample_long_config}[kind](i)
 
 
 def describe(w, L):
@@ -134,7 +159,7 @@ def test_sampled_configs_are_valid():
 @pytest.mark.parametrize("kind,i", CONFIGS)
 def test_sampled_config(kind, i):
     w, L = config(kind, i)
-    seed = (700 if kind == "kv" else 900) + i
+    seed = {"kv": 700, "latent": 900, "long": 1100}[kind] + i
     say(f"sampled {kind} config {i}: {describe(w, L)}")
     prefill_case(w, seed, L=L)
     steps = min(w["L_recent"] + 8, 48)
@@ -158,7 +183,8 @@ def varlen_draw(kind, i):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kind,i", [c for c in CONFIGS if c[0] == "latent" or c[1] < 24])
+@pytest.mark.parametrize("kind,i", [c for c in CONFIGS if c[0] == "latent" or
+                                   (c[0] == "kv" and c[1] < 24)])
 def test_sampled_config_varlen(kind, i):
     w, lens, rows, B_max, given_lse = varlen_draw(kind, i)
     say(f"sampled {kind} config {i}, varlen: {describe(w, max(lens))}")
