@@ -264,16 +264,17 @@ void direct_rowstat_kernel(PrefillArgs a) {
       // MFMAs; a block whose sum passed 2^OVER is redone after the loop
       auto tile = [&](auto mask) __attribute__((always_inline)) {
         float add[NQB];
-        bool redo = false;
+        float big = 0.f;  // the largest tile sum (terms are positive)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           const f32x4_t acc = logits(qb, mask);
-          add[qb] = 0.f;
+          add[qb] = fast_exp2(__builtin_fmaf(acc[0], sc, -m[qb]));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) add[qb] += fast_exp2(__builtin_fmaf(acc[r], sc, -m[qb]));
-          redo |= !(add[qb] <= OVER);
+          for (int r = 1; r < 4; ++r) add[qb] += fast_exp2(__builtin_fmaf(acc[r], sc, -m[qb]));
+          big = fmaxf(big, add[qb]);
         }
-        if (__builtin_amdgcn_ballot_w64(redo) != 0) {  // wave-uniform; rare once m settles
+        // wave-uniform; rare once m settles (an overflowed sum is +inf)
+        if (__builtin_amdgcn_ballot_w64(!(big <= OVER)) != 0) {
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) {
             const f32x4_t acc = logits(qb, mask);
