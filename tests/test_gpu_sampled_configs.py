@@ -6,7 +6,9 @@ part or none), batch and prompt length (stored as is, or compressed by a
 little or by a lot); and latent (MLA) configurations of 576-dim rows with
 the same spread of sizes.  Each configuration runs the prefill comparison
 (scores, selection, slot map, gathered rows) and a decode run long enough to
-wrap a short ring, against the oracle.  Most also build a packed batch of
+wrap a short ring (on every other configuration with rows idling or handing
+over a position past their count now and then), against the oracle; the
+long draws have more than 16384 middle keys per group.  Most also build a packed batch of
 prompts of drawn lengths (stored and compressed mixed, into drawn cache
 rows, with the log-sum-exp given on every other draw) through
 ss_prefill_compress_varlen, every request checked against the oracle.
@@ -118,6 +120,23 @@ def sample_long_config(i):
 
 
 N_LONG = 8
+def row_schedule(seed, B, L):
+    """Per-step positions of B rows that start at L tokens, as a continuous
+    batch runs them: each step a row is idle (pos = -1) with probability
+    0.2, else decodes its next token (pos = its token count); now and then
+    (probability 0.05) a row hands over a position past its count, which the
+    step must flag and still apply at that position."""
+    rng = np.random.default_rng(seed)
+    n = np.full(B, L, dtype=np.int64)
+
+    def positions(t):
+        u = rng.random(B)
+        pos = np.where(u < 0.2, -1, n + np.where(u > 0.95, rng.integers(1, 4, B), 0))
+        n[pos >= 0] = pos[pos >= 0] + 1
+        return pos
+    return positions
+
+
 CONFIGS = ([("kv", i) for i in range(N_CONFIGS)] + [("latent", i) for i in range(N_LATENT)]
            + [("long", i) for i in range(N_LONG)])
 
@@ -163,7 +182,8 @@ def test_sampled_config(kind, i):
     say(f"sampled {kind} config {i}: {describe(w, L)}")
     prefill_case(w, seed, L=L)
     steps = min(w["L_recent"] + 8, 48)
-    decode_case(w, L=L, steps=steps, seed=seed + 100, check_every=4)
+    positions = row_schedule(seed, w["B"], L) if i % 2 else None
+    decode_case(w, L=L, steps=steps, seed=seed + 100, check_every=4, positions=positions)
 
 
 def varlen_draw(kind, i):
