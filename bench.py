@@ -12,6 +12,9 @@ Llama-3.1-8B-shaped layers (16384 -> 4096 at batch 16; 131072 -> 32768 at
 batch 8) are measured the same way after the timed steps and reported under
 `other_workloads`; the continuous-batching mix (64 rows, C = 32768, 1000
 decode steps with four 65536-token admissions) under `continuous_batching`.
+Each of these, and the uncompressed-cache baseline, runs in a fresh child
+process (`--leg`): buffers allocated after others were freed in the same
+process decoded about 5% slower.
 
 Decode runs over `--replicas` distinct copies of the layer's cache in turn
 (step t uses copy t mod replicas), so consecutive decode steps do not find
@@ -32,6 +35,7 @@ import argparse
 import ctypes
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -372,11 +376,12 @@ def continuous_batching(ss, torch, synth, seed=5):
                     "rows x steps over the whole timed region, admissions included"}
 
 
-def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_s):
+def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R):
     """The same decode over a cache that keeps the whole prompt (C = L: the
     recent window widened to L - L_sink - K, so the prompt is stored as it is
     and every slot is valid), timed like the compressed decode: what the
-    fixed-size cache saves per decode step."""
+    fixed-size cache saves per decode step (the caller divides by the
+    compressed decode's launch time)."""
     B, L = w["B"], w["L"]
     wu = dict(w, L_recent=L - w["L_sink"] - w["K"])
     wu["C"] = L
@@ -410,7 +415,6 @@ def uncompressed_baseline(ss, torch, hip, w, cfg, inp, dec, n_dec, R, attn_s):
         "decode_step_us": round(1e6 * step_s, 2),
         "decode_attn_GBps": round(dec_b / step_s / 1e9, 1),
         "kv_bytes_ratio": round(L / w["C"], 3),
-        "decode_speedup_of_fixed_cache": round(step_s / attn_s, 3),
         "note": f"{n} decode launches over a cache holding all {L} prompt tokens",
     }
 
@@ -541,6 +545,42 @@ PUBLIC_KEYS = ("decode_tokens_per_s_per_layer", "decode_tokens_per_s_model", "de
                "decode_step_us", "prefill_compress_ms_per_layer", "roofline", "score_kernels")
 
 
+def run_leg(leg, ss, torch, synth, hip, R, n_dec=None):
+    """One extra measurement, alone in its process: another workload's steps
+    (2 timed, 8 warm-up), the continuous-batching run, or the uncompressed
+    baseline of a workload ("uncompressed:<workload>")."""
+    if leg == "continuous_batching":
+        return continuous_batching(ss, torch, synth)
+    if leg.startswith("uncompressed:"):
+        w = synth.workload(leg.split(":", 1)[1])
+        n = n_dec or w["steps"]
+        inp = synth.prefill_inputs(w, seed=2, device="cuda")
+        dec = synth.decode_inputs(w, seed=2, steps=n, device="cuda")
+        return uncompressed_baseline(ss, torch, hip, w, ss.make_config(**w), inp, dec, n, R)
+    wo = synth.workload(leg)
+    # 8 warm-up steps: in a fresh process the host needs about that long
+    # before it issues decode launches faster than llama8b_c4k's 47 us
+    # kernels complete (after 1 warm-up step the launches came 110-120 us
+    # apart)
+    ro = run_steps(ss, torch, synth, hip, wo, 2, 8, wo["steps"], R)
+    return dict({"config": describe(wo, wo["steps"], R)}, **{k: ro[k] for k in PUBLIC_KEYS})
+
+
+def leg_in_child(leg, R, n_dec):
+    """run_leg in a fresh child process (this process waits for it).  In one
+    process, decode over buffers allocated after another workload's were
+    freed ran about 5% slower than in a fresh process (llama8b_128k 158.9
+    against 166.1-166.4 us per launch, the latent layer 188 against 196 us):
+    each measurement gets the memory state of a process that allocates its
+    caches once, as a server does and as the profile runs do."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--leg", leg, "--replicas", str(R),
+           "--decode-steps", str(n_dec)]
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"bench leg {leg} failed with status {p.returncode}")
+    return json.loads(p.stdout.strip().splitlines()[-1])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -557,6 +597,10 @@ def main():
                     help="time the step only: skip the given-lse prefill, the varlen admission, "
                          "the other workloads, the continuous-batching run and the "
                          "uncompressed baseline (for profiling runs)")
+    ap.add_argument("--leg", default=None,
+                    help="run one extra measurement alone and print it as JSON: a workload "
+                         "name, continuous_batching or uncompressed:<workload> (the full "
+                         "bench runs each extra measurement this way, in a child process)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (a kernel of "
                          "known traffic, to calibrate FETCH_SIZE/WRITE_SIZE counters)")
@@ -582,11 +626,15 @@ def main():
         torch.mul(src, 1.0, out=dst)       # reads and writes exactly n*4 bytes
         torch.cuda.synchronize()
         del src, dst
+    R = max(1, args.replicas)
+    hip = HipEvents()
+    if args.leg is not None:
+        print(json.dumps(run_leg(args.leg, ss, torch, synth, hip, R, args.decode_steps)),
+              flush=True)
+        return
     w = synth.workload(args.workload)
     cfg = ss.make_config(**w)
     n_dec = args.decode_steps or w["steps"]
-    R = max(1, args.replicas)
-    hip = HipEvents()
     r = run_steps(ss, torch, synth, hip, w, args.steps, args.warmup, n_dec, R)
     inp, dec = r["inp"], r["dec"]
     res = {
@@ -615,29 +663,22 @@ def main():
     if not args.no_extras:
         res["given_lse"] = given_lse_prefill(ss, torch, w, cfg, inp)
         res["varlen_admission"] = varlen_admission(ss, torch, synth, w, cfg)
-    if not (args.no_uncompressed or args.no_extras):
-        torch.cuda.empty_cache()
-        res["uncompressed_baseline"] = uncompressed_baseline(
-            ss, torch, hip, w, cfg, inp, dec, n_dec, R, r["attn_avg_s"])
     if not args.no_cpu_baseline:
         cpu_inp = {k: (v[:16] if v is not None else None) for k, v in inp.items()}
         cpu_dec = {k: (v.cpu() if v is not None else None) for k, v in dec.items()}
+    attn_s = r["attn_avg_s"]
     del r, inp, dec
     torch.cuda.empty_cache()
+    # each further measurement in a fresh child process (see leg_in_child)
+    if not (args.no_uncompressed or args.no_extras):
+        u = leg_in_child(f"uncompressed:{w['name']}", R, n_dec)
+        u["decode_speedup_of_fixed_cache"] = round(u["decode_step_us"] / (1e6 * attn_s), 3)
+        res["uncompressed_baseline"] = u
     if not args.no_extras:
-        others = {}
-        for name in ("llama8b_c4k", "llama8b_128k", "deepseek_mla_128k"):
-            if name == w["name"]:
-                continue
-            wo = synth.workload(name)
-            ro = run_steps(ss, torch, synth, hip, wo, 2, 1, wo["steps"], R)
-            others[name] = dict({"config": describe(wo, wo["steps"], R)},
-                                **{k: ro[k] for k in PUBLIC_KEYS})
-            del ro
-            torch.cuda.empty_cache()
-        res["other_workloads"] = others
-        res["continuous_batching"] = continuous_batching(ss, torch, synth)
-        torch.cuda.empty_cache()
+        res["other_workloads"] = {
+            name: leg_in_child(name, R, synth.workload(name)["steps"])
+            for name in ("llama8b_c4k", "llama8b_128k", "deepseek_mla_128k") if name != w["name"]}
+        res["continuous_batching"] = leg_in_child("continuous_batching", R, n_dec)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, cpu_inp, cpu_dec)
     print(json.dumps(res), flush=True)
