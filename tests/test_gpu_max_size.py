@@ -10,7 +10,9 @@ Decode: one row and one kv-head of 64 dims hold 2^24 valid slots; one step
 oracle, which starts from an exact fp64 copy of the same cache.  A few
 planted keys far into the cache (and one at its middle) match the query and
 hold nearly all of the attention, so a slot offset that wrapped or lost its
-high bits would move the output by far more than the tolerance."""
+high bits would move the output by far more than the tolerance.  The same
+for the latent layout at 2^22 slots (4.5 GiB per row: past 32-bit byte
+offsets)."""
 import numpy as np
 import pytest
 import torch
@@ -88,3 +90,55 @@ def test_decode_at_the_largest_cache(dtype):
     assert np.array_equal(cache.v[0, 0, slot].double().cpu().numpy(), state.v[0, 0, slot])
     assert int(cache.slot_pos[0, 0, slot].item()) == C_MAX
     assert int(cache.n_tokens[0].item()) == C_MAX + 1
+
+
+def test_latent_decode_past_4gib_per_row():
+    # latent rows of 1152 bytes: at 2^22 slots one row's cache spans 4.5 GiB,
+    # past what 32-bit byte offsets reach.  The query lives in the last 64
+    # dims; the planted keys match it there (logit ~40, the random keys
+    # ~N(0, 0.75)) and carry constant values in the first 512 dims.
+    C = 1 << 22
+    S, K = 16, 48
+    w = synth.workload("deepseek_mla_128k", B=1, n_q_heads=8, L_sink=S, K=K,
+                       L_recent=C - S - K, rope_theta=0.0, rope_begin=0, rope_end=0)
+    assert w["C"] == C
+    say("latent decode at C = 2^22")
+    cfg = lib_config(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(79)
+    cache = ss.Cache(cfg, 1)
+    cache.k.copy_(torch.randn(cache.k.shape, generator=g, device="cuda"))
+    u = torch.zeros(576, device="cuda")
+    u[512:] = torch.randn(64, generator=g, device="cuda")
+    u *= 12.0 / u.norm()
+    planted = {C - 3: 2.0, C - (1 << 20) - 11: -1.0, C // 2 + 7: 0.5}
+    for slot, val in planted.items():
+        row = 4.0 * u
+        row[:512] = val
+        cache.k[0, 0, slot] = row.to(torch.bfloat16)
+    cache.slot_pos.copy_(torch.arange(C, dtype=torch.int32, device="cuda")[None, None])
+    cache.n_tokens.fill_(C)
+
+    state = oracle.CacheState(oracle_config(w), 1)
+    state.k = cache.k.double().cpu().numpy()
+    state.slot_pos = cache.slot_pos.cpu().numpy().astype(np.int64)
+    state.n_tokens = np.array([C], dtype=np.int64)
+
+    q = u.to(torch.bfloat16)[None, None].repeat(1, 8, 1).contiguous()     # [1, 8, 576]
+    k_new = torch.randn(1, 1, 576, generator=g, device="cuda").to(torch.bfloat16)
+    pos = torch.tensor([C], dtype=torch.int32, device="cuda")
+    out = torch.empty(1, 8, 512, dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ss.ss_decode_step(cfg, q, k_new, None, pos, cache, out, err)
+    ref, ref_err = oracle.decode_step(state, synth.to_f64(q.cpu()), synth.to_f64(k_new.cpu()),
+                                      None, np.array([C]))
+    torch.cuda.synchronize()
+    diff = np.abs(out.double().cpu().numpy() - ref).max()
+    say(f"  output mean {ref.mean():.4f} (planted rows alone: {np.mean(list(planted.values())):.4f}), "
+        f"max-abs {diff:.3g}")
+    assert diff <= OUT_TOL["bf16"]
+    assert not ref_err and int(err.item()) == 0
+    slot = oracle.ring_slot(C, S, K, C - S - K)
+    assert np.array_equal(cache.k[0, 0, slot].double().cpu().numpy(), state.k[0, 0, slot])
+    assert int(cache.slot_pos[0, 0, slot].item()) == C
+    assert int(cache.n_tokens[0].item()) == C + 1
