@@ -69,7 +69,9 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
  * Supported (d_qk, d_v, dtype): (64, 64, f32|bf16), (128, 128, f32|bf16),
  * (576, 512, bf16) with v_aliases_k = 1 (MLA absorbed latent; its rotary range,
  * if any, must start on a multiple of 8 dims and span a multiple of 16).  G = n_q_heads /
- * n_kv_heads must be an integer <= 16; G * W <= 256. */
+ * n_kv_heads must be an integer <= 16; G * W <= 256.  n_kv_heads, the cache's
+ * B_max and a prefill call's b are at most 65535 (they index launch grid
+ * dimensions): SS_ERR_UNSUPPORTED beyond, and the workspace sizes are 0. */
 typedef struct {
   int32_t n_q_heads;
   int32_t n_kv_heads;

@@ -10,6 +10,9 @@
 namespace {
 
 constexpr size_t ALIGN = 256;
+// Cache rows, requests and kv-heads index launch grid dimensions y / z,
+// whose extent is at most 65535.
+constexpr int MAX_GRID_YZ = 65535;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool supported_shape(const ss_config* c) {
@@ -44,7 +47,8 @@ ss_status check_config(const ss_config* c) {
   if (C > ss::MAX_CACHE_SLOTS) return SS_ERR_INVALID_ARG;
   if (c->dtype != SS_F32 && c->dtype != SS_BF16) return SS_ERR_INVALID_ARG;
   const int G = c->n_q_heads / c->n_kv_heads;
-  if (!supported_shape(c) || G > 16 || G * c->W > 256) return SS_ERR_UNSUPPORTED;
+  if (!supported_shape(c) || G > 16 || G * c->W > 256 || c->n_kv_heads > MAX_GRID_YZ)
+    return SS_ERR_UNSUPPORTED;
   if (c->rope_theta > 0.f && c->rope_end - c->rope_begin > 2 * ss::ROPE_MAX_PAIRS)
     return SS_ERR_UNSUPPORTED;
   return SS_OK;
@@ -188,13 +192,13 @@ int32_t ss_cache_slots(const ss_config* cfg) {
 }
 
 size_t ss_prefill_workspace_bytes(const ss_config* cfg, int32_t b, int32_t L) {
-  if (check_config(cfg) != SS_OK || b < 1 || L < 1) return 0;
+  if (check_config(cfg) != SS_OK || b < 1 || b > MAX_GRID_YZ || L < 1) return 0;
   const PrefillPlan p = plan_prefill(cfg, b, L);
   return p.compressed ? p.total : ALIGN;  // a non-zero size keeps the pointer rule uniform
 }
 
 size_t ss_decode_workspace_bytes(const ss_config* cfg, int32_t B_max) {
-  if (check_config(cfg) != SS_OK || B_max < 1) return 0;
+  if (check_config(cfg) != SS_OK || B_max < 1 || B_max > MAX_GRID_YZ) return 0;
   return plan_decode(cfg, B_max).total;
 }
 
@@ -203,6 +207,7 @@ ss_status ss_decode_workspace_init(const ss_config* cfg, int32_t B_max, void* ws
   const ss_status cs = check_config(cfg);
   if (cs != SS_OK) return cs;
   if (B_max < 1) return SS_ERR_INVALID_ARG;
+  if (B_max > MAX_GRID_YZ) return SS_ERR_UNSUPPORTED;
   const DecodePlan p = plan_decode(cfg, B_max);
   if (ws == nullptr || ws_bytes < p.total) return SS_ERR_WORKSPACE;
   int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.off_cnt);
@@ -233,6 +238,7 @@ ss_status prefill_impl(const ss_config* cfg, const void* q_obs, const void* k, c
       misaligned(cache->v) || misaligned(ws))
     return SS_ERR_INVALID_ARG;
   if (rows == nullptr && b > cache->B_max) return SS_ERR_INVALID_ARG;
+  if (b > MAX_GRID_YZ) return SS_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(cu) & 3) != 0) return SS_ERR_INVALID_ARG;
   const int C = cache_slots(cfg);
   const bool compressed = L > C;  // with cu: some request may be compressed
@@ -316,6 +322,7 @@ ss_status decode_impl(const ss_config* cfg, const void* q, const void* k_new, co
   if (misaligned(q) || misaligned(k_new) || misaligned(v_new) || misaligned(cache->k) ||
       misaligned(cache->v) || (!use_static && misaligned(ws)))
     return SS_ERR_INVALID_ARG;
+  if (cache->B_max > MAX_GRID_YZ) return SS_ERR_UNSUPPORTED;
   const DecodePlan p =
       plan_decode(cfg, cache->B_max, use_static ? ss::STATIC_SCRATCH_PARTIALS_OFF : 0);
   if (use_static) {

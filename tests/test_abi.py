@@ -157,3 +157,22 @@ def test_status_strings():
     assert ss.status_string(ss.SS_OK) == "ok"
     assert "workspace" in ss.status_string(ss.SS_ERR_WORKSPACE)
     assert ss.status_string(99) == "unknown status"
+
+
+def test_row_counts_beyond_the_grid_limit_are_unsupported():
+    # cache rows and requests index launch grid dimensions (at most 65535)
+    cfg = _cfg()
+    lib = ss.lib()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: the checks fail first
+    assert ss.ss_decode_workspace_bytes(cfg, 65535) > 0
+    assert ss.ss_decode_workspace_bytes(cfg, 65536) == 0
+    assert ss.ss_prefill_workspace_bytes(cfg, 65536, 100) == 0
+    big = ss.ss_cache(fake, fake, fake, fake, 65536)
+    assert lib.ss_decode_step(ctypes.byref(cfg), fake, fake, fake, fake, ctypes.byref(big), fake,
+                              None, fake, 1 << 40, None) == ss.SS_ERR_UNSUPPORTED
+    assert lib.ss_decode_workspace_init(ctypes.byref(cfg), 65536, fake, 1 << 40,
+                                        None) == ss.SS_ERR_UNSUPPORTED
+    assert lib.ss_prefill_compress(ctypes.byref(cfg), fake, fake, fake, 65536, 100, fake,
+                                   ctypes.byref(big), None, None, None, fake, 1 << 40,
+                                   None) == ss.SS_ERR_UNSUPPORTED
+    assert ss.ss_decode_workspace_bytes(_cfg(n_q_heads=65536, n_kv_heads=65536), 1) == 0
