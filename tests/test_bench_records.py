@@ -30,3 +30,24 @@ def test_committed_decode_records_name_existing_sources():
         assert rec["sources"] and all(os.path.exists(os.path.join(ROOT, s)) for s in rec["sources"])
         assert rec["traffic_bytes"] > 0 and rec["rocprof_avg_us"] > 0
         assert len(rec["source_digest"]) == 64
+
+
+def test_extra_leg_runs_in_a_child_and_its_failure_is_reported(monkeypatch):
+    calls = []
+
+    class Done:
+        def __init__(self, rc, out):
+            self.returncode, self.stdout = rc, out
+
+    def fake_run(cmd, stdout=None, text=None):
+        calls.append(cmd)
+        if "continuous_batching" in cmd:
+            return Done(-9, "")
+        return Done(0, 'some log line\n{"decode_step_us": 47.0}\n')
+
+    monkeypatch.setattr(bench.subprocess, "run", fake_run)
+    assert bench.leg_in_child("llama8b_c4k", 4, 256) == {"decode_step_us": 47.0}
+    assert "error" in bench.leg_in_child("continuous_batching", 4, 512)
+    # a fresh interpreter running this same script, one leg
+    assert all(c[1].endswith("bench.py") and c[2:4] == ["--leg", c[3]] for c in calls)
+    assert calls[0][3] == "llama8b_c4k" and "--replicas" in calls[0]
