@@ -1,7 +1,8 @@
 """Host-side checks of bench.py's bookkeeping (no GPU): the digest that ties a
 committed rocprof record to the kernel sources ignores comments and blank
-space but not code, and every committed decode record names sources that
-exist."""
+space but not code, every committed decode record names sources that exist,
+and the extra measurements run as child processes whose failure is reported
+in the line instead of ending the run."""
 import json
 import os
 
