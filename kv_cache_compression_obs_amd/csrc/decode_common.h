@@ -1,4 +1,4 @@
-// Helpers shared by the decode kernels (decode.hip, decode_mla.hip).
+// Helpers shared by the decode kernels (decode.hip, decode_ring.hip, decode_mla.hip).
 #pragma once
 
 #include "common.h"
