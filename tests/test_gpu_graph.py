@@ -1,7 +1,8 @@
 """Both library calls enqueue only kernels on the caller's stream (no
 allocation, no memset, no host synchronisation), so they can be captured into
-a HIP graph.  Each test captures the calls once, then replays the graph three
-times; between replays the program does its own eager work (restoring the
+a HIP graph: for bf16 heads of 128 dims, fp32 heads of 64 dims and latent
+rows (each decode kernel and each family of score passes).  Each test
+captures the calls once, then replays the graph three times; between replays the program does its own eager work (restoring the
 cache, poisoning the outputs) and synchronises, and every replay must match
 the eager run bit for bit (the kernels are deterministic).  The library keeps
 no global state either: decode on two streams at once, each with its own
@@ -16,25 +17,35 @@ from parity import lib_config, say
 pytestmark = pytest.mark.gpu
 
 W = dict(B=4, L_sink=16, K=200, L_recent=512)  # llama8b_c4k shapes, C = 728
+# the three decode kernels and both families of score passes: bf16 heads of
+# 128 dims (ring decode), fp32 heads of 64 dims, latent rows
+GRAPH_CASES = {
+    "llama8b_c4k": (dict(W), 2000, 3000),
+    "tiny_fp32": (dict(B=4), 512, 512),
+    "deepseek_mla_128k": (dict(W), 2000, 3000),
+}
 
 
 def _restore(dst: ss.Cache, src: ss.Cache):
     dst.k.copy_(src.k)
-    dst.v.copy_(src.v)
+    if dst.v is not None:
+        dst.v.copy_(src.v)
     dst.slot_pos.copy_(src.slot_pos)
     dst.n_tokens.copy_(src.n_tokens)
 
 
 def _same_cache(a: ss.Cache, b: ss.Cache):
-    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+    assert torch.equal(a.k, b.k) and (a.v is None or torch.equal(a.v, b.v))
     assert torch.equal(a.slot_pos, b.slot_pos) and torch.equal(a.n_tokens, b.n_tokens)
 
 
-def test_decode_steps_replay_in_a_graph():
-    w = synth.workload("llama8b_c4k", **W)
+@pytest.mark.parametrize("name", sorted(GRAPH_CASES))
+def test_decode_steps_replay_in_a_graph(name):
+    kw, L, _ = GRAPH_CASES[name]
+    w = synth.workload(name, **kw)
     cfg = lib_config(w)
-    B, L, T = w["B"], 2000, 4
-    say(f"graph decode: {T} steps, B={B}, C={w['C']}")
+    B, T = w["B"], 4
+    say(f"graph decode {name}: {T} steps, B={B}, C={w['C']}")
     inp = synth.prefill_inputs(w, 70, device="cuda", L=L)
     base = ss.Cache(cfg, B)
     ss.ss_prefill_compress(cfg, inp["q_obs"], inp["k"], inp["v"], base)
@@ -47,9 +58,10 @@ def test_decode_steps_replay_in_a_graph():
 
     ref = base.clone()
     ref_out = [torch.empty(shape, dtype=dt, device="cuda") for _ in range(T)]
+    vn = [dec["v_new"][t] if dec["v_new"] is not None else None for t in range(T)]
     for t in range(T):
-        ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], dec["v_new"][t], pos[t], ref,
-                          ref_out[t], err, ws=ws)
+        ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], vn[t], pos[t], ref, ref_out[t], err,
+                          ws=ws)
     torch.cuda.synchronize()
 
     cache = base.clone()
@@ -57,8 +69,8 @@ def test_decode_steps_replay_in_a_graph():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for t in range(T):
-            ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], dec["v_new"][t], pos[t], cache,
-                              out[t], err, ws=ws)
+            ss.ss_decode_step(cfg, dec["q"][t], dec["k_new"][t], vn[t], pos[t], cache, out[t],
+                              err, ws=ws)
     for rep in range(3):
         _restore(cache, base)
         for o in out:
@@ -72,11 +84,13 @@ def test_decode_steps_replay_in_a_graph():
     assert int(err.item()) == 0
 
 
-def test_prefill_replays_in_a_graph():
-    w = synth.workload("llama8b_c4k", **W)
+@pytest.mark.parametrize("name", sorted(GRAPH_CASES))
+def test_prefill_replays_in_a_graph(name):
+    kw, _, L = GRAPH_CASES[name]
+    w = synth.workload(name, **kw)
     cfg = lib_config(w)
-    B, L = w["B"], 3000
-    say(f"graph prefill: B={B}, L={L}, C={w['C']}")
+    B = w["B"]
+    say(f"graph prefill {name}: B={B}, L={L}, C={w['C']}")
     inp = synth.prefill_inputs(w, 72, device="cuda", L=L)
     ws = torch.empty(ss.ss_prefill_workspace_bytes(cfg, B, L), dtype=torch.uint8, device="cuda")
     sel = torch.empty(B, w["n_kv_heads"], w["K"], dtype=torch.int32, device="cuda")
