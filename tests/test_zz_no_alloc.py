@@ -53,6 +53,8 @@ def test_noalloc_matches_workspace_decode_shrinking_inputs():
     _pair(small, B=3, L=200, seed=72, steps=3)            # 3 x 256 slots, below capacity
     lat = synth.workload("deepseek_mla_128k", B=2, L_sink=8, K=120, L_recent=384)
     _pair(lat, B=2, L=1500, seed=73, steps=2)             # latent (MLA) shape
+    tiny = synth.workload("tiny_fp32", B=3)
+    _pair(tiny, B=3, L=400, seed=74, steps=3)             # fp32 heads (register-tile kernel)
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
