@@ -133,7 +133,9 @@ ss_status ss_decode_workspace_init(const ss_config* cfg, int32_t B_max, void* ws
  *   k      [b, n_kv_heads, L, d_qk]  prompt keys (post-RoPE)
  *   v      [b, n_kv_heads, L, d_v]   prompt values (NULL when v_aliases_k)
  *   rows   device int32 [b]: destination cache row of each request, or NULL
- *          for rows 0 .. b-1 (continuous-batching admission into chosen rows)
+ *          for rows 0 .. b-1 (continuous-batching admission into chosen rows);
+ *          distinct (two requests into one row leave it undefined); a row
+ *          outside [0, B_max) is skipped
  *   raw_out    optional device float [b, n_kv_heads, m], m = L - L_sink - L_recent:
  *              the middle-key scores (written only when L > C)
  *   pooled_out optional device float [b, n_kv_heads, m]: the pooled scores
