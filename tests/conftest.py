@@ -31,7 +31,8 @@ def pytest_collection_modifyitems(config, items):
 def pytest_sessionfinish(session, exitstatus):
     # the tie-band counts of the selection comparisons (GPU parity tests):
     # per test, the groups compared, |A| in total and at most, and the in-band
-    # swaps (out-of-band differences fail the test itself)
+    # swaps (out-of-band differences fail the test itself); written as
+    # tie_band.json into the directory SS_TIE_BAND_DIR names, if it is set
     try:
         import parity
     except Exception:  # pragma: no cover
@@ -48,7 +49,9 @@ def pytest_sessionfinish(session, exitstatus):
         a["band_max"] = max(a["band_max"], r["band"])
         a["swaps_total"] += r["swaps"]
         a["swaps_max"] = max(a["swaps_max"], r["swaps"])
-    out = os.path.join(ROOT, "gpurun_out")
+    out = os.environ.get("SS_TIE_BAND_DIR")
+    if not out:
+        return
     try:
         os.makedirs(out, exist_ok=True)
         with open(os.path.join(out, "tie_band.json"), "w") as f:

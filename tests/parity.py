@@ -27,7 +27,7 @@ OUT_TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 # one record per compared (request, kv-head) selection: the test, |A| (keys
 # within the band of the K-th pooled score) and the in-band swaps; written to
-# gpurun_out/tie_band.json at the end of the session (tests/conftest.py)
+# $SS_TIE_BAND_DIR/tie_band.json at the end of the session (tests/conftest.py)
 TIE_LOG = []
 
 
