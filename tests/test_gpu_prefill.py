@@ -47,6 +47,26 @@ def test_prefill_admits_into_chosen_rows():
     assert (cache.slot_pos[0] == -1).all() and (cache.slot_pos[2] == -1).all()
 
 
+def test_prefill_skips_rows_outside_the_cache():
+    # requests aimed at rows -1 and B_max leave the cache untouched; the one
+    # aimed at row 1 is built as usual, and row 0 keeps its contents
+    w = synth.workload("tiny_fp32", B=3)
+    inp = synth.prefill_inputs(w, 6, device="cuda")
+    rows = torch.tensor([-1, 1, 2], dtype=torch.int32, device="cuda")
+    from kv_cache_compression_obs_amd import snapstream as ss
+    from parity import lib_config
+    cache = ss.Cache(lib_config(w), 2)
+    cache.k.fill_(3.0)
+    cache.v.fill_(-3.0)
+    cache.slot_pos.fill_(-5)
+    cache.n_tokens.fill_(7)
+    res = run_lib_prefill(w, inp, cache=cache, rows=rows)
+    for h in range(2):
+        check_prefill_group(w, inp, res, 1, h, row=1)
+    assert (cache.k[0] == 3.0).all() and (cache.v[0] == -3.0).all()
+    assert (cache.slot_pos[0] == -5).all() and int(cache.n_tokens[0].item()) == 7
+
+
 def test_prefill_llama8b_c4k_full_shape():
     # 16 requests x 8 kv-heads, 16384 -> 4096; every group against the oracle
     prefill_case(synth.workload("llama8b_c4k"), 11)
