@@ -157,6 +157,24 @@ struct Geo {
     return acc;
   }
 
+  // Logits of the tile against every q-block, the MFMAs issued slice by
+  // slice over all q-blocks: NQB independent accumulators between two MFMAs
+  // of one chain, where logits() runs each q-block's chain back to back.
+  // The same MFMAs in the same order per q-block, so the same logits.
+  template <int NQB>
+  static __device__ __forceinline__ void logits_all(f32x4_t (&acc)[NQB], const u32x4_t (&av)[NJ],
+                                                    const u32x4_t (&qv)[NQB][NJ]) {
+    using MM = Mma<T>;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < Piece<T>::N; ++e)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          acc[qb] = MM::mma(Piece<T>::get(av[j], e), Piece<T>::get(qv[qb][j], e),
+                            (j == 0 && e == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[qb]);
+  }
+
   // Byte offsets of this lane's A-operand units in a ring slot.
   static __device__ __forceinline__ void a_offsets(int (&aoff)[NJ], int col, int qg) {
 #pragma unroll
@@ -336,9 +354,13 @@ void direct_rowstat_kernel(PrefillArgs a) {
 // recent region): no causal mask.  Per tile and lane: for each of the lane's
 // 4 keys, sum over the q-blocks of 2^(x - M) * w (rows past G*W have zero
 // queries and w = 0: exact zeros); then over the 16 columns of the lane row
-// by DPP.  The sums of a wave's keys are staged in LDS and written once its
-// loads have drained (no store may sit between the loads whose count the
-// wave waits for).
+// by DPP.  The loop is pipelined over tiles: the next tile's MFMAs (slice by
+// slice over all q-blocks) are issued among this tile's exponentials, so no
+// exponential waits on an MFMA issued just before it (with the key loads
+// switched off, 91 -> 62 us over 16 x 8 groups of 14272 middle keys; 1-3%
+// with them on, where the key stream bounds the pass).  The sums of a
+// wave's keys are staged in LDS and written once its loads have drained (no
+// store may sit between the loads whose count the wave waits for).
 template <typename T, int D, int NQB, int NW, int NS>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW * (NS * Geo<T, D>::TB + DIRECT_STAGE_KEYS * 4) <= 80 * 1024
@@ -381,23 +403,33 @@ void direct_columns_kernel(PrefillArgs a) {
 
   if (ntile > 0) {
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
+    for (int i = 0; i < NS; ++i)
       GG::issue_tile(ring + i * GG::TB, kbase, first + i * 16 * NW, k1, lane, lo);
+    // the logits of tile 0; every later tile's logits are computed one
+    // iteration early, their MFMAs issued among the previous tile's
+    // exponentials
+    wait_loads<(NS - 1) * GG::NI>();
+    u32x4_t av[GG::NJ];
+    GG::read_a(av, ring, aoff);
+    f32x4_t acc[NQB];
+    GG::template logits_all<NQB>(acc, av, q);
     for (int it = 0; it < ntile; ++it) {
       const int t0 = first + it * 16 * NW;
-      wait_loads<(NS - 2) * GG::NI>();
-      GG::issue_tile(ring + ((it + NS - 1) % NS) * GG::TB, kbase, t0 + (NS - 1) * 16 * NW, k1,
-                     lane, lo);
-      u32x4_t av[GG::NJ];
-      GG::read_a(av, ring + (it % NS) * GG::TB, aoff);
+      // slot it % NS held tile it, whose fragments are in registers (the
+      // MFMAs that read them waited for the LDS reads); tile it + NS goes
+      // there, then tile it + 1 must have landed (tiles past the last one
+      // are clamped re-reads: their logits are unused)
+      GG::issue_tile(ring + (it % NS) * GG::TB, kbase, t0 + NS * 16 * NW, k1, lane, lo);
+      wait_loads<(NS - 1) * GG::NI>();
+      GG::read_a(av, ring + ((it + 1) % NS) * GG::TB, aoff);
       float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        const f32x4_t acc = GG::logits(av, q[qb]);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          cs[r] = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[r], sc, nM[qb])), w[qb], cs[r]);
+          cs[r] = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[qb][r], sc, nM[qb])), w[qb], cs[r]);
       }
+      GG::template logits_all<NQB>(acc, av, q);
       // over the 16 columns: halves keep keys {0,1} / {2,3}, quarters one
       // key, then two quad steps; lane (col, qg) ends with key 4*qg + col/4
       const float sa = b3 ? cs[0] : cs[2], sb = b3 ? cs[1] : cs[3];
