@@ -5,8 +5,9 @@ largest group the score kernels take (G = 16, G*W = 256 rows), rotary
 embedding over part of the head (decode rotates dims 32..95 of 128) or over
 every dim of an fp32 head, and pooling windows at and past the select
 kernel's LDS staging limit (also on a group long enough for the select to be
-split over several workgroups) or wider than the whole middle region, and a
-batch of 2048 rows.  Each
+split over several workgroups) or wider than the whole middle region, middle
+regions of 201 and 17 keys on the 128-row score kernels, and a batch of 2048
+rows.  Each
 configuration runs the prefill comparison (scores, selection, slot map,
 gathered rows) and a decode run across the ring wrap (outputs, written rows,
 n_tokens) against the oracle."""
@@ -40,6 +41,11 @@ CASES = {
     # a wide batch: 2048 rows of a 64-slot cache (grids 2048 deep in the
     # row dimension, one short split per row)
     "wide_batch_2048_rows": (TINY, dict(B=2048, L_sink=4, K=16, L_recent=44), 100),
+    # short middle regions on the 128-row bf16 score kernels: 201 middle
+    # keys (a ragged last tile; each wave owns fewer tiles than its ring
+    # holds) and 17 (one full tile and a one-key tile: two waves own no tile)
+    "middle_201_keys": (SMALL, dict(B=2, L_sink=16, K=200, L_recent=512), 729),
+    "middle_17_keys": (SMALL, dict(B=2, L_sink=16, K=10, L_recent=512), 545),
     # 39472 middle keys: the select work is split over parts of the group,
     # and the 515-wide window is pooled straight from the raw scores
     "pool_515_split_select": (SMALL, dict(B=1, n_q_heads=8, n_kv_heads=2, pool=515, L_sink=16,
