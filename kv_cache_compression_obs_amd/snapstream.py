@@ -118,9 +118,11 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int:
+def _stream(stream, t) -> int:
+    """The raw handle of `stream`, by default the current stream of the
+    device that holds tensor t (the device the call's buffers live on)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(t.get_device())
     return stream.cuda_stream
 
 
@@ -169,7 +171,7 @@ def ss_decode_workspace_bytes(cfg: ss_config, B_max: int) -> int:
 def ss_decode_workspace_init(cfg: ss_config, B_max: int, ws, stream=None) -> None:
     _check(ws, "ws", torch.uint8)
     st = lib().ss_decode_workspace_init(ctypes.byref(cfg), int(B_max), _ptr(ws), ws.numel(),
-                                        _stream(stream))
+                                        _stream(stream, ws))
     if st != SS_OK:
         raise SnapStreamError(st, "ss_decode_workspace_init")
 
@@ -246,7 +248,7 @@ def ss_prefill_compress(cfg: ss_config, q_obs, k, v, cache: Cache, rows=None, ra
                          device=k.device)
     cs = cache.struct()
     tail = (_ptr(rows), ctypes.byref(cs), _ptr(raw_out), _ptr(pooled_out), _ptr(sel_out),
-            _ptr(ws), ws.numel(), _stream(stream))
+            _ptr(ws), ws.numel(), _stream(stream, k))
     head = (ctypes.byref(cfg), _ptr(q_obs), _ptr(k), _ptr(v), b, L)
     if lse is not None:
         _check(lse, "lse", torch.float32, (b, Hq, cfg.W))
@@ -298,7 +300,7 @@ def ss_prefill_compress_varlen(cfg: ss_config, q_obs, k, v, cu_seqlens, max_L: i
     cs = cache.struct()
     args = (ctypes.byref(cfg), _ptr(q_obs), _ptr(k), _ptr(v), b, _ptr(cu_seqlens), int(max_L),
             _ptr(lse), _ptr(rows), ctypes.byref(cs), _ptr(raw_out), _ptr(pooled_out),
-            _ptr(sel_out), _ptr(ws), ws.numel(), _stream(stream))
+            _ptr(sel_out), _ptr(ws), ws.numel(), _stream(stream, k))
     if events is None:
         st = lib().ss_prefill_compress_varlen(*args)
     else:
@@ -340,7 +342,7 @@ def ss_decode_step(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, out, err_
         ws = decode_workspace(cfg, cache.B_max, q.device)
     cs = cache.struct()
     args = (ctypes.byref(cfg), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), ctypes.byref(cs),
-            _ptr(out), _ptr(err_flag), _ptr(ws), ws.numel(), _stream(stream))
+            _ptr(out), _ptr(err_flag), _ptr(ws), ws.numel(), _stream(stream, q))
     if events is None:
         st = lib().ss_decode_step(*args)
     else:
@@ -357,6 +359,6 @@ def ss_decode_step_noalloc(cfg: ss_config, q, k_new, v_new, pos, cache: Cache, o
     cs = cache.struct()
     st = lib().ss_decode_step_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k_new), _ptr(v_new),
                                       _ptr(pos), ctypes.byref(cs), _ptr(out), _ptr(err_flag),
-                                      _stream(stream))
+                                      _stream(stream, q))
     if st != SS_OK:
         raise SnapStreamError(st, "ss_decode_step_noalloc")
