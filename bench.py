@@ -547,8 +547,9 @@ PUBLIC_KEYS = ("decode_tokens_per_s_per_layer", "decode_tokens_per_s_model", "de
 
 def run_leg(leg, ss, torch, synth, hip, R, n_dec=None):
     """One extra measurement, alone in its process: another workload's steps
-    (2 timed, 8 warm-up), the continuous-batching run, or the uncompressed
-    baseline of a workload ("uncompressed:<workload>")."""
+    (2 timed, 8 warm-up) and its one-pass prefill (given log-sum-exp), the
+    continuous-batching run, or the uncompressed baseline of a workload
+    ("uncompressed:<workload>")."""
     if leg == "continuous_batching":
         return continuous_batching(ss, torch, synth)
     if leg.startswith("uncompressed:"):
@@ -562,8 +563,13 @@ def run_leg(leg, ss, torch, synth, hip, R, n_dec=None):
     # before it issues decode launches faster than llama8b_c4k's 47 us
     # kernels complete (after 1 warm-up step the launches came 110-120 us
     # apart)
-    ro = run_steps(ss, torch, synth, hip, wo, 2, 8, wo["steps"], R)
-    return dict({"config": describe(wo, wo["steps"], R)}, **{k: ro[k] for k in PUBLIC_KEYS})
+    inp = synth.prefill_inputs(wo, seed=2, device="cuda")
+    ro = run_steps(ss, torch, synth, hip, wo, 2, 8, wo["steps"], R, inp=inp)
+    res = dict({"config": describe(wo, wo["steps"], R)}, **{k: ro[k] for k in PUBLIC_KEYS})
+    del ro
+    torch.cuda.empty_cache()
+    res["given_lse"] = given_lse_prefill(ss, torch, wo, ss.make_config(**wo), inp)
+    return res
 
 
 def leg_in_child(leg, R, n_dec):
